@@ -1,0 +1,18 @@
+"""CPU oracle for the exact attention forward pass (float64, numpy).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import it; the HIP library and
+its Python binding never do, and the oracle never imports them.
+
+  * ``ref``   - the plain definition, score matrix materialised.
+  * ``tiled`` - the Q-outer online-softmax recurrence with tile sizes as
+                arguments, used to pin the recurrence to the definition.
+"""
+
+from .ref import as_f64, scores_ref, probabilities_ref, attention_ref, attention_rows_ref
+from .tiled import tiled_ref
+
+__all__ = [
+    "as_f64", "scores_ref", "probabilities_ref", "attention_ref",
+    "attention_rows_ref", "tiled_ref",
+]
