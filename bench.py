@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward on one MI355X.
+
+One step = one full forward pass (``fa_fwd`` through the C ABI: one kernel
+launch) over the long-context workload B=1, H=64, N=16384, d=128, bf16,
+causal, with Q/K/V already resident in HBM.  Prints ONE JSON line:
+
+  metric / value / unit   attention forward TFLOP/s, counting 4*B*H*N^2*d
+                          FLOPs halved for causal, over the timed steps
+  roofline                the kernel against the bf16 dense matrix-core peak
+                          (achieved = FLOPs per launch / average launch time
+                          from HIP events on the launch stream)
+  cpu_baseline            the fp64 CPU oracle timed on a bounded sample of
+                          the same workload on this host's cores
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak (2.5 PFLOP/s)
+DEFAULT_WORKLOAD = "longctx_n16384_d128_causal"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(w, q, k, v, target_s):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same
+    workload: whole heads, every query row computed on its own, until about
+    ``target_s`` seconds of CPU work have been done."""
+    import numpy as np
+    import torch
+    from oracle import attention_rows_ref  # CPU baseline leg only
+
+    rows = np.arange(w.N)
+    flops = 0.0
+    heads = 0
+    nrows = 0
+    t0 = time.perf_counter()
+    el = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            qh, kh, vh = (x[b, h].to(torch.float64).numpy() for x in (q, k, v))
+            for i in range(0, w.N, 256):
+                sel = rows[i:i + 256]
+                attention_rows_ref(qh, kh, vh, w.scale, w.causal, sel)
+                keys = (sel + 1) if w.causal else np.full(sel.size, w.N)
+                flops += 4.0 * float(keys.sum()) * w.d
+                nrows += sel.size
+            heads += 1
+            el = time.perf_counter() - t0
+            if el >= target_s:
+                break
+        if el >= target_s:
+            break
+    cores = len(os.sched_getaffinity(0))
+    blas_threads = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas_threads = max([x.get("num_threads", 1) for x in info if x.get("user_api") == "blas"] or [1])
+    except Exception:
+        pass
+    threads = blas_threads if blas_threads else 1
+    return {
+        "value": flops / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(min(threads, cores)),
+        "kind": "oracle",
+        "sample": (f"{heads} whole head(s) ({nrows} query rows) of {w.name}, each row computed on its own "
+                   f"by the fp64 numpy oracle (attention_rows_ref), {el:.1f} s wall; "
+                   f"{cores} host cores visible, BLAS threads {blas_threads}"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the forward pass shards over "
+              "(batch, head) and query tiles with no exchange, so there is no multi-GPU run to time.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import io_aware_exact_fa1_amd as fa
+    import workloads
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    fa.load_library()
+    w = workloads.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log(f"[bench] generating inputs {w.name} B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
+    q, k, v = workloads.make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, w.k_mult)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    entry = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_f32
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step():
+        st = entry(qd, kd, vd, o, lse, w.B, w.H, w.N, w.d, w.scale, int(w.causal), sh)
+        if st != fa.FA_OK:
+            raise fa.FaError(st, "fa_fwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    # timed region: K steps between synchronisations; HIP events on the
+    # launch stream bracket every launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    avg_ms = sum(launch_ms) / len(launch_ms)
+    med_ms = launch_ms[len(launch_ms) // 2]
+    ms_per_step = wall * 1e3 / args.steps
+    tflop = w.flops / 1e12
+    value = tflop / (ms_per_step / 1e3)
+    achieved = tflop / (avg_ms / 1e3)
+    log(f"[bench] {w.name}: wall {ms_per_step:.3f} ms/step, kernel avg {avg_ms:.3f} ms "
+        f"(median {med_ms:.3f}, min {launch_ms[0]:.3f}) -> {achieved:.1f} TFLOP/s "
+        f"= {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 dense peak")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            with open(TRAFFIC_FILE) as f:
+                t = json.load(f)
+            if t.get("workload") == w.name:
+                traffic = t.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle on a sample (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        log(f"[bench] cpu baseline {cpu['value'] * 1e3:.3f} GFLOP/s ({cpu['sample']})")
+
+    out = {
+        "metric": "attn fwd TFLOP/s + % bf16 MFMA peak, N=16K d=128 causal (1 MI355X)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "scale": w.scale, "flops_per_step": w.flops, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

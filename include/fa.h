@@ -1,0 +1,120 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) exact-attention forward library.
+ *
+ * The library computes, for every (batch b, head h), the exact attention
+ * forward pass over square self-attention inputs:
+ *
+ *     O   = softmax(scale * Q K^T [+ causal mask]) V
+ *     LSE = row-wise logsumexp(scale * Q K^T [+ causal mask])   (natural log)
+ *
+ * without ever forming the N x N score matrix in memory: Q is split into
+ * row tiles, every K/V tile streams through on-chip LDS, and a running row
+ * max m and sum-exp l (online softmax) rescale the partial output, which is
+ * written to HBM once as O = a / l together with LSE = m + ln l.
+ *
+ * Definitions followed:
+ *   - Problem statement (Q, K, V in, O out, O = softmax(QK^T / sqrt d) V):
+ *     "FlashAttention V1" (infra.bea.ai), section "3. The Algorithm";
+ *     "15. FlashAttention" (inference.shantanugoel.com), section "The score
+ *     matrix is the problem".
+ *   - The LSE output, m + log(l) per query row, written with O:
+ *     "Lecture 3 - FlashAttention-1 Algorithm" (jared-hpc.com), section
+ *     "The forward loop"; the logsumexp reading of it: "FlashAttention：从
+ *     IO-Aware Attention 到 GPU Work Partitioning" (blog.euler0525.cn),
+ *     section "减少 Non-Matmul FLOPs".
+ *   - Causal rule (key j visible to query i iff j <= i) and the masked,
+ *     never-read tail of N not a multiple of the tile: "15. FlashAttention",
+ *     section "The kernel".
+ *   - fp32 inputs computed in true fp32, not a reduced-precision matrix
+ *     mode: "15. FlashAttention", section "The kernel" (the input_precision
+ *     note).
+ *
+ * Layout (all entry points): Q, K, V and O are dense, contiguous, row-major
+ * [B, H, N, d] arrays; element (b, h, n, e) sits at ((b*H + h)*N + n)*d + e.
+ * LSE is a dense fp32 [B, H, N] array.  All pointers are DEVICE pointers
+ * (memory of the current HIP device).
+ *
+ * Ownership: the caller owns every buffer.  The library allocates nothing,
+ * frees nothing and keeps no pointer after the call returns.  O and LSE are
+ * written in full; they must not overlap Q, K, V or each other.
+ *
+ * Streams: work is enqueued on `stream` (0 = the null stream) and the call
+ * returns without synchronising; the caller synchronises.
+ *
+ * Errors: every entry point returns FA_OK (0) or one of the FA_ERR_* codes
+ * below.  Argument errors are detected on the host before any launch, and
+ * then nothing is enqueued and nothing is written.  B*H*N == 0 is a no-op
+ * that returns FA_OK.  FA_ERR_LAUNCH reports the HIP error of the launch
+ * (from hipGetLastError, which may also carry an earlier, unrelated error of
+ * the calling thread).
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* a null pointer while B*H*N > 0                 */
+    FA_ERR_SHAPE = 2,     /* B, H or N negative, or sizes overflow the grid */
+    FA_ERR_HEAD_DIM = 3,  /* d not in {64, 128}                             */
+    FA_ERR_SCALE = 4,     /* scale is NaN or infinite                       */
+    FA_ERR_ALIAS = 5,     /* O or LSE overlaps Q, K, V or each other        */
+    FA_ERR_LAUNCH = 6,    /* the HIP launch reported an error               */
+    FA_ERR_ALIGN = 7      /* a pointer is not aligned to 16 bytes           */
+};
+
+/*
+ * Exact attention forward, bf16 inputs and output, fp32 statistics.
+ *
+ *   q, k, v : const bf16 [B, H, N, d] device arrays (bf16 = IEEE binary32
+ *             with the low 16 bits dropped), 16-byte aligned.
+ *   o       : bf16 [B, H, N, d] device array, written: O rounded to bf16
+ *             with round-to-nearest-even.
+ *   lse     : float [B, H, N] device array, written: natural-log logsumexp
+ *             of the scaled, masked scores of each query row.
+ *   B, H, N : batch, heads, sequence length (N >= 1 when B*H > 0; any N,
+ *             tiles need not divide it).
+ *   d       : head dimension, 64 or 128.
+ *   scale   : finite multiplier of Q K^T (usually 1/sqrt(d)); any sign.
+ *   causal  : 0 = no mask; nonzero = key j is visible to query i iff j <= i.
+ *   stream  : HIP stream to enqueue on.
+ *
+ * Arithmetic: Q K^T and P V run on bf16 matrix cores with fp32 accumulation;
+ * the row max, the exponentials (base 2 with log2(e) folded into the scale),
+ * the row sums, the running output and LSE are fp32; P is rounded to bf16
+ * only as the operand of P V, while l sums the unrounded values.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/*
+ * Exact attention forward for fp32 inputs and output, computed in true fp32
+ * (fp32 products and sums on the vector ALUs; no reduced-precision matrix
+ * mode).  Arguments, layout, errors and semantics as fa_fwd, with q, k, v
+ * and o fp32 [B, H, N, d] device arrays (16-byte aligned).
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_strerror(int status);
+
+/*
+ * Host-side argument check of fa_fwd / fa_fwd_f32 without any HIP call:
+ * returns the status those entry points would return before launching.
+ * elem_bytes is 2 (bf16) or 4 (fp32).  Lets tests and callers validate on
+ * machines without a GPU.
+ */
+int fa_check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  int B, int H, int N, int d, float scale, int causal, int elem_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

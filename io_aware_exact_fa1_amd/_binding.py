@@ -1,0 +1,138 @@
+"""ctypes binding of the C ABI in ``include/fa.h`` (argument marshalling only).
+
+The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_strerror`` and ``fa_check_args``
+have the names and argument order of the C entry points; tensors are passed
+as their device pointers and streams as HIP stream handles.  Every step of
+the computation runs in the HIP library: there is no fallback path, and a
+missing or unloadable library raises.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libfa_mi355x.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+
+FA_OK = 0
+FA_ERR_NULL = 1
+FA_ERR_SHAPE = 2
+FA_ERR_HEAD_DIM = 3
+FA_ERR_SCALE = 4
+FA_ERR_ALIAS = 5
+FA_ERR_LAUNCH = 6
+FA_ERR_ALIGN = 7
+
+EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_check_args")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A nonzero status returned by the HIP library."""
+
+    def __init__(self, status, where):
+        self.status = int(status)
+        super().__init__(f"{where}: status {status}: {fa_strerror(status)}")
+
+
+def load_library(path=None):
+    """Load the HIP library (once).  torch is imported first so that the
+    library binds to the HIP runtime torch already loaded."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    import torch  # noqa: F401  (must precede the CDLL: one HIP runtime per process)
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"HIP library {p} is not built: run `python -m io_aware_exact_fa1_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(p)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    sig = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+    lib.fa_fwd.argtypes = sig
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_f32.argtypes = sig
+    lib.fa_fwd_f32.restype = i
+    lib.fa_strerror.argtypes = [i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i]
+    lib.fa_check_args.restype = i
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
+    """C ``fa_fwd``: bf16 q, k, v, o and fp32 lse; returns the status code."""
+    return load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N),
+                                 int(d), float(scale), int(causal), _stream(stream))
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
+    """C ``fa_fwd_f32``: fp32 q, k, v, o and lse; returns the status code."""
+    return load_library().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                     int(N), int(d), float(scale), int(causal), _stream(stream))
+
+
+def fa_strerror(status):
+    return load_library().fa_strerror(int(status)).decode()
+
+
+def fa_check_args(q, k, v, o, lse, B, H, N, d, scale, causal, elem_bytes):
+    return load_library().fa_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                        int(N), int(d), float(scale), int(causal), int(elem_bytes))
+
+
+def forward(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
+    """Allocate O / LSE with torch (if not given), call the C entry point for
+    the dtype of q, raise FaError on a nonzero status; returns (O, LSE).
+
+    q, k, v: CUDA tensors [B, H, N, d] of one dtype (bfloat16 or float32).
+    """
+    import math
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors")
+    if q.shape != k.shape or q.shape != v.shape or q.dim() != 4:
+        raise ValueError("q, k and v must share one [B, H, N, d] shape")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    B, H, N, d = q.shape
+    q, k, v = (x.contiguous() for x in (q, k, v))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        if q.dtype == torch.bfloat16:
+            st = fa_fwd(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+            where = "fa_fwd"
+        elif q.dtype == torch.float32:
+            st = fa_fwd_f32(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
+            where = "fa_fwd_f32"
+        else:
+            raise ValueError(f"unsupported dtype {q.dtype}")
+    if st != FA_OK:
+        raise FaError(st, where)
+    return out, lse

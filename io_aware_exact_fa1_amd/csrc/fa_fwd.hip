@@ -1,0 +1,516 @@
+// Exact attention forward for MI355X (gfx950, CDNA4): HIP kernels + C ABI.
+//
+// What is computed (per batch b, head h; square self-attention):
+//   O = softmax(scale * Q K^T [causal: key j visible to query i iff j <= i]) V
+//   LSE = m + ln(l), the natural-log logsumexp of each query row's scores.
+// Sources: "Lecture 3 - FlashAttention-1 Algorithm" (jared-hpc.com), section
+// "The forward loop (Algorithm 1 from the FA1 paper)": Q-outer, KV-inner loop
+// with running m and l, O and LSE written once per query tile.  "15.
+// FlashAttention" (inference.shantanugoel.com), section "Online softmax:
+// normalize as you go" (unnormalised accumulator a, O = a / l) and section
+// "The kernel" (one program per query block of one (batch, head), the causal
+// loop bound, the safe reference for a row with no visible key yet, masked
+// tail loads, fp32 statistics with p cast to the value type for P V).
+// "FlashAttention：从 IO-Aware Attention 到 GPU Work Partitioning"
+// (blog.euler0525.cn), sections "Sequence Parallelism" (query tiles are the
+// parallel work units), "Warp Work Partitioning" (each wave owns its own
+// query rows; no cross-wave reduction of O) and "Tile Size 与 Causal
+// Attention" (tiles above the diagonal are skipped, only diagonal tiles are
+// masked element by element).
+//
+// gfx950 design (one workgroup = NW wave64s, each wave owns 32 query rows):
+//  * The score tile is computed transposed, S^T = K Q^T, with
+//    v_mfma_f32_32x32x16_bf16.  In the MFMA accumulator layout a lane then
+//    holds ONE query (lane % 32) and 16 keys per 32-key block, so the row
+//    max / row sum are in-lane reductions plus one v_permlane32_swap, and the
+//    per-row rescale factor is a per-lane scalar.
+//  * The same accumulator registers, rounded to bf16, are directly the B
+//    operand of O^T = V^T P^T (no data movement for P).  The V^T operand is
+//    read from a row-major V tile in LDS with ds_read_b64_tr_b16, the gfx950
+//    LDS transpose load.
+//  * K and V tiles are copied HBM -> LDS with global_load_lds_dwordx4
+//    (no VGPR staging), double-buffered, with an XOR swizzle of the 16-byte
+//    chunks so that both the K reads (8 rows x 16 B) and the transposed V
+//    reads (4 rows x 32 B) hit distinct LDS banks.
+//  * Exponentials are exp2 with log2(e) folded into the scale; m, l and the
+//    output accumulator stay in fp32 registers; O is divided by l once.
+//  * Work units are query tiles (causal: a heavy tile paired with a light
+//    one, so every unit costs the same); the 1-D grid is remapped so that
+//    each XCD runs a contiguous range of units, i.e. the query tiles of the
+//    same heads, which then share K/V through that XCD's L2.
+//
+// The fp32 entry point runs a plain vector-ALU kernel (true fp32 products
+// and sums), one thread per query row.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Tile configuration of the bf16 kernel.
+template <int D_, int NW_, int BC_>
+struct Cfg {
+  static constexpr int D = D_;             // head dimension
+  static constexpr int NW = NW_;           // waves per workgroup
+  static constexpr int BC = BC_;           // keys per K/V tile (B_c)
+  static constexpr int BR = 32 * NW;       // query rows per tile (B_r)
+  static constexpr int ROWB = D * 2;       // bytes of one K/V row
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;     // rows per 1 KB wave-wide copy
+  static constexpr int TILEB = BC * ROWB;  // bytes of one K (or V) tile
+  static constexpr int NINST = TILEB / 1024;
+  static constexpr int KB = D / 16;        // 16-deep k-steps of Q K^T
+  static constexpr int DB = D / 32;        // 32-dim output blocks
+  static constexpr int SB = BC / 32;       // 32-key score blocks
+  static constexpr int PB = BC / 16;       // 16-key k-steps of P V
+  static_assert(NINST % NW == 0, "copy instructions must split evenly over waves");
+  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+};
+
+// XOR swizzle of the 16-byte chunk index within a K/V row (rows are 128 or
+// 256 bytes).  Eight consecutive rows map one chunk to eight distinct
+// positions; four consecutive rows map two adjacent chunks to eight
+// distinct positions.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Symmetric reductions across the two 32-lane halves (lane l and l ^ 32):
+// v_permlane32_swap(x, x) yields {x[l % 32], x[l % 32 + 32]} in every lane.
+__device__ __forceinline__ float half_max(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ void wait_vm_all() {
+  // s_waitcnt vmcnt(0): all vector-memory operations of this wave done,
+  // including the global -> LDS copies.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Issue the HBM -> LDS copies of one K and one V tile (keys k0 .. k0+BC-1).
+// Rows past the end of the sequence are clamped to row N-1: they are never
+// read from HBM past the array, hold finite values, and are masked to -inf
+// (K) / multiplied by an exact 0 (V).
+template <class C>
+__device__ __forceinline__ void load_kv_tile(unsigned char LDS_AS* dst, const uint16_t* kh,
+                                             const uint16_t* vh, int k0, int N, int w, int lane) {
+#pragma unroll
+  for (int ii = 0; ii < C::NINST / C::NW; ++ii) {
+    const int t = w * (C::NINST / C::NW) + ii;
+    const int row = t * C::RPI + lane / C::CPR;
+    const int chunk = (lane % C::CPR) ^ swz(row);
+    const int grow = min(k0 + row, N - 1);
+    const size_t off = (size_t)grow * C::D + (size_t)chunk * 8;
+    __builtin_amdgcn_global_load_lds((const void*)(kh + off), (void LDS_AS*)(dst + t * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(vh + off),
+                                     (void LDS_AS*)(dst + C::TILEB + t * 1024), 16, 0, 0);
+  }
+}
+
+// One K/V tile for one wave: S^T = K Q^T, online softmax, acc += V^T P^T.
+template <class C, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void attend_tile(const unsigned char LDS_AS* kt, const unsigned char LDS_AS* vt,
+                                            const bf16x8 (&qr)[C::KB], f32x16 (&acc)[C::DB], float& m,
+                                            float& lsum, int k0, int qw0, int N, float c, int lane) {
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  // ---- S^T = K_j Q_i^T (fp32 accumulation of exact bf16 products)
+  f32x16 s[C::SB];
+#pragma unroll
+  for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[sb][i] = 0.f;
+  const int ksw = swz(l32);
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb) {
+      const int row = sb * 32 + l32;
+      const bf16x8 a = *(const bf16x8 LDS_AS*)(kt + row * C::ROWB + 16 * ((2 * kb + h) ^ ksw));
+      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[kb], s[sb], 0, 0, 0);
+    }
+  }
+
+  // ---- mask: keys past N, and keys after the query when causal
+  if (MASK) {
+    const int query = qw0 + l32;
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + sb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        const bool vis = key < N && (!CAUSAL || key <= query);
+        s[sb][i] = vis ? s[sb][i] : -INFINITY;
+      }
+  }
+
+  // ---- row max (in-lane over this half's keys, then across the halves)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
+  mx = half_max(mx);
+  const float mxs = (mx == -INFINITY) ? -INFINITY : mx * c;  // c >= 0
+  const float m_new = fmaxf(m, mxs);
+  const float mref = (m_new == -INFINITY) ? 0.f : m_new;      // safe reference
+  const float alpha = __builtin_amdgcn_exp2f(m - mref);       // 0 when m = -inf
+
+  // ---- P = exp2(S*c - m_ref), row sum from the unrounded values
+  float rs = 0.f;
+#pragma unroll
+  for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c, -mref));
+      if (MASK) p = (s[sb][i] == -INFINITY) ? 0.f : p;
+      rs += p;
+      s[sb][i] = p;
+    }
+  lsum = alpha * lsum + rs;
+
+  // ---- rescale the running output only when some row's max moved
+  if (__builtin_amdgcn_ballot_w64(m_new != m)) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+  }
+  m = m_new;
+
+  // ---- P as the bf16 B operand of O^T += V^T P^T (same registers, in order)
+  bf16x8 pb[C::PB];
+#pragma unroll
+  for (int kb2 = 0; kb2 < C::PB; ++kb2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pb[kb2][j] = (__bf16)s[kb2 >> 1][8 * (kb2 & 1) + j];
+
+  // ---- V^T operand via LDS transpose loads.  Lane (g = lane/16, r, b):
+  // reads V row (16*kb2 + 4h + r [+8]), dims (32*db + 16*(g%2) + 4b .. +3);
+  // after the transpose, lane l holds V[16*kb2 + 4h + 0..3 (+8)][32*db + l%32].
+  const int vr = 4 * h + ((lane >> 2) & 3);
+  const int vsw = swz(vr);
+  const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+  for (int kb2 = 0; kb2 < C::PB; ++kb2) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const int dim = 32 * db + vdim;
+      const unsigned char LDS_AS* pa =
+          vt + (16 * kb2 + vr) * C::ROWB + 16 * ((dim >> 3) ^ vsw) + 2 * (dim & 7);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)pa);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(pa + 8 * C::ROWB));
+      const bf16x4 lob = __builtin_bit_cast(bf16x4, lo);
+      const bf16x4 hib = __builtin_bit_cast(bf16x4, hi);
+      const bf16x8 a = __builtin_shufflevector(lob, hib, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb2], acc[db], 0, 0, 0);
+    }
+  }
+}
+
+template <class C, bool CAUSAL>
+__global__ void __launch_bounds__(C::NW * 64)
+fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                   const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
+                   int N, int T_r, int units_per_head, int num_units, int per_xcd, float c,
+                   unsigned int qsign) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * C::TILEB];
+  unsigned char LDS_AS* sm = (unsigned char LDS_AS*)smem;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+
+  // Workgroups are dispatched round-robin over the 8 XCDs: block b runs on
+  // XCD b % 8.  Give XCD x the contiguous units [x*per_xcd, (x+1)*per_xcd).
+  const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (u >= num_units) return;
+  const int bh = u / units_per_head;
+  const int ur = u - bh * units_per_head;
+  int tiles[2];
+  int ntiles = 1;
+  if (CAUSAL) {
+    tiles[0] = T_r - 1 - ur;  // heavy tile first
+    tiles[1] = ur;
+    ntiles = (tiles[1] < tiles[0]) ? 2 : 1;
+  } else {
+    tiles[0] = ur;
+    tiles[1] = ur;
+  }
+
+  const size_t hoff = (size_t)bh * (size_t)N * C::D;
+  const uint16_t* qh = q + hoff;
+  const uint16_t* kh = k + hoff;
+  const uint16_t* vh = v + hoff;
+
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int q0 = tiles[ti] * C::BR;
+    const int qw0 = q0 + w * 32;
+
+    // Q_i rows as the B operand of S^T = K Q^T: lane holds query qw0 + l%32,
+    // dims 16*kb + 8*(l/32) .. +7.  Rows past N are clamped (never stored).
+    bf16x8 qr[C::KB];
+    {
+      const int row = min(qw0 + l32, N - 1);
+      const uint16_t* src = qh + (size_t)row * C::D + 8 * h;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        u32x4 x = *(const u32x4*)(src + 16 * kb);
+        x ^= qsign;  // exact sign flip when the caller's scale is negative
+        qr[kb] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+
+    float m = -INFINITY, lsum = 0.f;
+    f32x16 acc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+
+    const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
+    const int nkv = (kv_end + C::BC - 1) / C::BC;
+
+    load_kv_tile<C>(sm, kh, vh, 0, N, w, lane);
+    wait_vm_all();
+    __syncthreads();
+
+    for (int j = 0; j < nkv; ++j) {
+      if (j + 1 < nkv)
+        load_kv_tile<C>(sm + ((j + 1) & 1) * 2 * C::TILEB, kh, vh, (j + 1) * C::BC, N, w, lane);
+      const int k0 = j * C::BC;
+      const unsigned char LDS_AS* kt = sm + (j & 1) * 2 * C::TILEB;
+      const unsigned char LDS_AS* vt = kt + C::TILEB;
+      const bool active = !CAUSAL || k0 <= qw0 + 31;  // some key visible to this wave
+      if (active) {
+        const bool need_mask = (k0 + C::BC > N) || (CAUSAL && k0 + C::BC - 1 > qw0);
+        if (need_mask)
+          attend_tile<C, CAUSAL, true>(kt, vt, qr, acc, m, lsum, k0, qw0, N, c, lane);
+        else
+          attend_tile<C, CAUSAL, false>(kt, vt, qr, acc, m, lsum, k0, qw0, N, c, lane);
+      }
+      wait_vm_all();
+      __syncthreads();
+    }
+
+    // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
+    const float lt = half_sum(lsum);
+    const float inv = 1.f / lt;
+    const int query = qw0 + l32;
+    if (query < N) {
+      uint16_t* orow = o + hoff + (size_t)query * C::D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[db][4 * a + e] * inv);
+          *(u32x2*)(orow + 32 * db + 8 * a + 4 * h) = __builtin_bit_cast(u32x2, ov);
+        }
+      if (h == 0) lse[(size_t)bh * N + query] = (m + __log2f(lt)) * kLn2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: true fp32 arithmetic on the vector ALUs, one thread per query.
+constexpr int F32_BQ = 64;  // queries per workgroup (one wave)
+constexpr int F32_BK = 32;  // keys per LDS tile
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(64)
+fa_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+                  float* __restrict__ o, float* __restrict__ lse, int N, float c) {
+  __shared__ float ks[F32_BK][D];
+  __shared__ float vs[F32_BK][D];
+  const int t = threadIdx.x;
+  const int q0 = blockIdx.x * F32_BQ;
+  const int bh = blockIdx.y;
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const int query = q0 + t;
+  const int qrow = min(query, N - 1);
+
+  float qv[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) qv[e] = q[hoff + (size_t)qrow * D + e];
+  float acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) acc[e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const int kv_end = CAUSAL ? min(N, q0 + F32_BQ) : N;
+  for (int k0 = 0; k0 < kv_end; k0 += F32_BK) {
+    __syncthreads();
+    for (int idx = t; idx < F32_BK * D; idx += 64) {
+      const int r = idx / D, e = idx % D;
+      const int grow = min(k0 + r, N - 1);
+      ks[r][e] = k[hoff + (size_t)grow * D + e];
+      vs[r][e] = v[hoff + (size_t)grow * D + e];
+    }
+    __syncthreads();
+    float s[F32_BK];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < F32_BK; ++j) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) dot = fmaf(qv[e], ks[j][e], dot);
+      const int key = k0 + j;
+      const bool vis = key < N && (!CAUSAL || key <= query);
+      s[j] = vis ? dot * c : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m, mx);
+    const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m - mref);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < D; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int j = 0; j < F32_BK; ++j) {
+      const float p = (s[j] == -INFINITY) ? 0.f : exp2f(s[j] - mref);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(p, vs[j][e], acc[e]);
+    }
+    m = m_new;
+  }
+  if (query < N) {
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int e = 0; e < D; ++e) o[hoff + (size_t)query * D + e] = acc[e] * inv;
+    lse[(size_t)bh * N + query] = (m + log2f(l)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+int check(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int H,
+          int N, int d, float scale, int elem_bytes) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const long long rows = (long long)B * H * N;
+  if (rows == 0) return FA_OK;
+  if ((long long)B * H > (1LL << 30) || rows > (1LL << 40)) return FA_ERR_SHAPE;
+  // grid size: query tiles of at least 32 rows per (b, h), padded to 8
+  if ((long long)B * H * ((N + 31) / 32) > (1LL << 30)) return FA_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
+  if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
+  const size_t nb = (size_t)rows * d * elem_bytes;
+  const size_t lb = (size_t)rows * sizeof(float);
+  if (overlaps(o, nb, q, nb) || overlaps(o, nb, k, nb) || overlaps(o, nb, v, nb) ||
+      overlaps(lse, lb, q, nb) || overlaps(lse, lb, k, nb) || overlaps(lse, lb, v, nb) ||
+      overlaps(lse, lb, o, nb))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+template <class C, bool CAUSAL>
+void launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                 float c, unsigned qsign, hipStream_t stream) {
+  const int T_r = (N + C::BR - 1) / C::BR;
+  const int units_per_head = CAUSAL ? (T_r + 1) / 2 : T_r;
+  const int num_units = B * H * units_per_head;
+  const int per_xcd = (num_units + 7) / 8;
+  const int grid = per_xcd * 8;
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL>), dim3(grid), dim3(C::NW * 64), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, T_r,
+                     units_per_head, num_units, per_xcd, c, qsign);
+}
+
+template <int D, bool CAUSAL>
+void launch_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
+                float c, hipStream_t stream) {
+  dim3 grid((N + F32_BQ - 1) / F32_BQ, B * H);
+  hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, stream, q, k, v, o, lse, N, c);
+}
+
+using CfgD128 = Cfg<128, 4, 64>;
+using CfgD64 = Cfg<64, 4, 64>;
+
+}  // namespace
+
+extern "C" int fa_check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             int B, int H, int N, int d, float scale, int causal, int elem_bytes) {
+  (void)causal;
+  if (elem_bytes != 2 && elem_bytes != 4) return FA_ERR_SHAPE;
+  return check(q, k, v, o, lse, B, H, N, d, scale, elem_bytes);
+}
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                      int d, float scale, int causal, hipStream_t stream) {
+  const int st = check(q, k, v, o, lse, B, H, N, d, scale, 2);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * N == 0) return FA_OK;
+  // Scores are formed as |scale| * (sign(scale) Q) K^T: a negative scale flips
+  // the sign bit of every Q element (exact), so the kernel sees c >= 0.
+  const unsigned qsign = (scale < 0.f) ? 0x80008000u : 0u;
+  const float c = fabsf(scale) * kLog2e;
+  if (d == 128) {
+    if (causal) launch_bf16<CfgD128, true>(q, k, v, o, lse, B, H, N, c, qsign, stream);
+    else launch_bf16<CfgD128, false>(q, k, v, o, lse, B, H, N, c, qsign, stream);
+  } else {
+    if (causal) launch_bf16<CfgD64, true>(q, k, v, o, lse, B, H, N, c, qsign, stream);
+    else launch_bf16<CfgD64, false>(q, k, v, o, lse, B, H, N, c, qsign, stream);
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+                          int N, int d, float scale, int causal, hipStream_t stream) {
+  const int st = check(q, k, v, o, lse, B, H, N, d, scale, 4);
+  if (st != FA_OK) return st;
+  if ((long long)B * H * N == 0) return FA_OK;
+  const float c = scale * kLog2e;
+  if (d == 128) {
+    if (causal) launch_f32<128, true>(q, k, v, o, lse, B, H, N, c, stream);
+    else launch_f32<128, false>(q, k, v, o, lse, B, H, N, c, stream);
+  } else {
+    if (causal) launch_f32<64, true>(q, k, v, o, lse, B, H, N, c, stream);
+    else launch_f32<64, false>(q, k, v, o, lse, B, H, N, c, stream);
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer argument";
+    case FA_ERR_SHAPE: return "invalid or too large shape (B, H, N)";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension (need 64 or 128)";
+    case FA_ERR_SCALE: return "scale is not finite";
+    case FA_ERR_ALIAS: return "output buffers overlap inputs or each other";
+    case FA_ERR_LAUNCH: return "HIP kernel launch failed";
+    case FA_ERR_ALIGN: return "pointer not aligned (16 bytes for q/k/v/o, 4 for lse)";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,94 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launch).
+
+The library must load, export every entry point ``include/fa.h`` declares,
+and reject bad arguments on the host before any HIP call.
+"""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import io_aware_exact_fa1_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(["fa_check_args", "fa_fwd", "fa_fwd_f32", "fa_strerror"])
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = fa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    raw = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared_functions():
+        assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value, name
+
+
+def test_strerror_covers_codes():
+    for code in range(0, 8):
+        s = fa.fa_strerror(code)
+        assert s and s != "unknown status", code
+    assert fa.fa_strerror(99) == "unknown status"
+
+
+# Fake device addresses: aligned, disjoint, never dereferenced (argument checks
+# return before any HIP call).
+Q, K, V, O, L = (0x10000000 * (i + 1) for i in range(5))
+
+
+@pytest.mark.parametrize("elem", [2, 4])
+def test_check_args_ok(elem):
+    assert fa.fa_check_args(Q, K, V, O, L, 2, 3, 100, 64, 0.125, 1, elem) == fa.FA_OK
+    assert fa.fa_check_args(Q, K, V, O, L, 1, 1, 1, 128, -2.0, 0, elem) == fa.FA_OK
+
+
+@pytest.mark.parametrize("args,code", [
+    ((Q, K, V, O, L, -1, 1, 8, 64, 1.0, 0), fa.FA_ERR_SHAPE),
+    ((Q, K, V, O, L, 1, -1, 8, 64, 1.0, 0), fa.FA_ERR_SHAPE),
+    ((Q, K, V, O, L, 1, 1, -8, 64, 1.0, 0), fa.FA_ERR_SHAPE),
+    ((Q, K, V, O, L, 1, 1, 8, 32, 1.0, 0), fa.FA_ERR_HEAD_DIM),
+    ((Q, K, V, O, L, 1, 1, 8, 96, 1.0, 0), fa.FA_ERR_HEAD_DIM),
+    ((Q, K, V, O, L, 1, 1, 8, 64, math.nan, 0), fa.FA_ERR_SCALE),
+    ((Q, K, V, O, L, 1, 1, 8, 64, math.inf, 0), fa.FA_ERR_SCALE),
+    ((None, K, V, O, L, 1, 1, 8, 64, 1.0, 0), fa.FA_ERR_NULL),
+    ((Q, K, V, O, None, 1, 1, 8, 64, 1.0, 0), fa.FA_ERR_NULL),
+    ((Q + 8, K, V, O, L, 1, 1, 8, 64, 1.0, 0), fa.FA_ERR_ALIGN),
+    ((Q, K, V, O, L + 2, 1, 1, 8, 64, 1.0, 0), fa.FA_ERR_ALIGN),
+    ((Q, K, V, Q, L, 1, 1, 8, 64, 1.0, 0), fa.FA_ERR_ALIAS),
+    ((Q, K, V, O, O + 64, 1, 1, 8, 64, 1.0, 0), fa.FA_ERR_ALIAS),
+    ((Q, K, V, O, L, 1 << 20, 1 << 20, 8, 64, 1.0, 0), fa.FA_ERR_SHAPE),
+])
+def test_check_args_errors(args, code):
+    assert fa.fa_check_args(*args, 2) == code
+
+
+def test_entry_points_reject_bad_args_before_any_launch():
+    # These return on the host before touching HIP, so they are safe without a GPU.
+    assert fa.fa_fwd(Q, K, V, O, L, 1, 1, 8, 80, 1.0, 0, 0) == fa.FA_ERR_HEAD_DIM
+    assert fa.fa_fwd_f32(Q, K, V, O, L, 1, 1, 8, 64, math.nan, 0, 0) == fa.FA_ERR_SCALE
+    assert fa.fa_fwd(None, K, V, O, L, 1, 1, 8, 64, 1.0, 0, 0) == fa.FA_ERR_NULL
+
+
+def test_empty_problem_is_a_noop():
+    # B*H*N == 0: FA_OK with no launch, even with null pointers.
+    assert fa.fa_fwd(None, None, None, None, None, 0, 4, 16, 64, 1.0, 1, 0) == fa.FA_OK
+    assert fa.fa_fwd_f32(None, None, None, None, None, 2, 4, 0, 128, 1.0, 0, 0) == fa.FA_OK
+
+
+def test_forward_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(x, x, x)
