@@ -44,7 +44,25 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-cal", action="store_true",
+                   help="run only a plain device copy of 1 GiB (5 times), to calibrate the HBM "
+                        "byte counters (FETCH_SIZE / WRITE_SIZE) of a profiler run")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size: its FETCH_SIZE and
+    WRITE_SIZE per dispatch, against 1 GiB each way, give the scale of the
+    byte counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[copy-cal] copied {n} bytes x5")
 
 
 def cpu_baseline(w, q, k, v, target_s):
@@ -103,6 +121,10 @@ def main():
               "(batch, head) and query tiles with no exchange, so there is no multi-GPU run to time.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_cal:
+        copy_calibration()
+        return
 
     import torch
     import io_aware_exact_fa1_amd as fa

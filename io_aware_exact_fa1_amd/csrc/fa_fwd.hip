@@ -47,6 +47,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa.h"
 
 namespace {
@@ -61,14 +63,25 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Exponent reference of the fast kernel.  Each row's reference m is fixed
+// at the max of its first key tile.  While no later score exceeds it by more
+// than kSlack (log2 units), the unnormalised weights p = exp2(s*c - m) stay
+// <= 2^kSlack, l <= N * 2^kSlack < 2^79 and acc cannot overflow for
+// |V| < 2^49; since O = acc / l and LSE = m + log2 l use one common m, the
+// result equals the running-max recurrence in exact arithmetic (the
+// recurrence holds for any common reference; the running max only bounds
+// the exponents).  A wave whose rows jump further marks its LSE rows with
+// NaN and is recomputed by the exact-rescaling kernel.
+constexpr float kSlack = 48.0f;
 
 // ---------------------------------------------------------------------------
 // Tile configuration of the bf16 kernel.
-template <int D_, int NW_, int BC_>
+template <int D_, int NW_, int BC_, int WPE_>
 struct Cfg {
   static constexpr int D = D_;             // head dimension
   static constexpr int NW = NW_;           // waves per workgroup
   static constexpr int BC = BC_;           // keys per K/V tile (B_c)
+  static constexpr int WPE = WPE_;         // waves per SIMD the register budget is sized for
   static constexpr int BR = 32 * NW;       // query rows per tile (B_r)
   static constexpr int ROWB = D * 2;       // bytes of one K/V row
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
@@ -83,11 +96,30 @@ struct Cfg {
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 };
 
-// XOR swizzle of the 16-byte chunk index within a K/V row (rows are 128 or
-// 256 bytes).  Eight consecutive rows map one chunk to eight distinct
-// positions; four consecutive rows map two adjacent chunks to eight
-// distinct positions.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// XOR swizzle of the 16-byte chunk index within a K/V row: chunk c of row r
+// is stored at chunk position c ^ swz(r).  Chosen for the two LDS read
+// patterns of the kernel, with 64 banks of 4 bytes (256 bytes per cycle):
+//  * K operand (ds_read_b128): 16 lanes read one chunk of 16 consecutive rows;
+//  * V operand (ds_read_b64_tr_b16): 32 lanes read 4 consecutive chunks of
+//    4 consecutive rows.
+// d = 128 (one row = 256 bytes = all banks): the 16 rows need 16 distinct
+// positions, and the 4 rows need distinct values in bits 2-3.  d = 64 (two
+// rows per 256 bytes): rows of equal parity need 8 distinct positions, and
+// rows r, r+2 of a 4-row group must differ in bit 2.
+#ifndef FA_SWZ
+#define FA_SWZ 1
+#endif
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+#if FA_SWZ == 0
+  return ((r & 3) << 1) | ((r >> 2) & 1);
+#elif FA_SWZ == 1
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+#else
+  return 0;
+#endif
+}
 
 // Symmetric reductions across the two 32-lane halves (lane l and l ^ 32):
 // v_permlane32_swap(x, x) yields {x[l % 32], x[l % 32 + 32]} in every lane.
@@ -117,7 +149,7 @@ __device__ __forceinline__ void load_kv_tile(unsigned char LDS_AS* dst, const ui
   for (int ii = 0; ii < C::NINST / C::NW; ++ii) {
     const int t = w * (C::NINST / C::NW) + ii;
     const int row = t * C::RPI + lane / C::CPR;
-    const int chunk = (lane % C::CPR) ^ swz(row);
+    const int chunk = (lane % C::CPR) ^ swz<C::D>(row);
     const int grow = min(k0 + row, N - 1);
     const size_t off = (size_t)grow * C::D + (size_t)chunk * 8;
     __builtin_amdgcn_global_load_lds((const void*)(kh + off), (void LDS_AS*)(dst + t * 1024), 16, 0, 0);
@@ -127,41 +159,62 @@ __device__ __forceinline__ void load_kv_tile(unsigned char LDS_AS* dst, const ui
 }
 
 // One K/V tile for one wave: S^T = K Q^T, online softmax, acc += V^T P^T.
-template <class C, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void attend_tile(const unsigned char LDS_AS* kt, const unsigned char LDS_AS* vt,
+// MASK: the tile may hold keys past N or, when causal, keys after some
+// query of the wave (masked to -inf, i.e. weight exactly 0).
+// EXACT = false (fast kernel): fixed reference, no rescaling; returns true
+// in the lanes of a row whose score exceeds its reference by more than
+// kSlack.  EXACT = true (recompute kernel): m is the running max and l and
+// acc are rescaled by exp2(m_old - m_new) on every tile.
+template <class C, bool CAUSAL, bool MASK, bool EXACT>
+__device__ __forceinline__ bool attend_tile(const unsigned char LDS_AS* kt, const unsigned char LDS_AS* vt,
                                             const bf16x8 (&qr)[C::KB], f32x16 (&acc)[C::DB], float& m,
                                             float& lsum, int k0, int qw0, int N, float c, int lane) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
+  // ---- K operand: lane reads row (32*sb + l%32), dims 16*kb + 8*(l/32) .. +7
+  const unsigned char LDS_AS* krow = kt + l32 * C::ROWB;
+  const int kf = swz<C::D>(l32);
+  auto load_k = [&](int kb, int sb) -> bf16x8 {
+    return *(const bf16x8 LDS_AS*)(krow + sb * 32 * C::ROWB + 16 * ((2 * kb + h) ^ kf));
+  };
+  // ---- V^T operand via LDS transpose loads.  Lane (g = l/16, r, b) reads V
+  // row (16*kb2 + 4h + r [+8]), dims (32*db + 16*(g%2) + 4b .. +3); after
+  // the transpose, lane l holds V[16*kb2 + 4h + 0..3 (+8)][32*db + l%32].
+  const int vr = 4 * h + ((lane >> 2) & 3);
+  const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int vf0 = swz<C::D>(vr), vf1 = swz<C::D>(vr + 8);
+  auto load_v = [&](int kb2, int db) -> bf16x8 {
+    const int dim = 32 * db + vdim;
+    const unsigned char LDS_AS* base = vt + (16 * kb2 + vr) * C::ROWB + 2 * (dim & 7);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (i16x4 LDS_AS*)(base + 16 * ((dim >> 3) ^ vf0)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (i16x4 LDS_AS*)(base + 8 * C::ROWB + 16 * ((dim >> 3) ^ vf1)));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1, 2,
+                                   3, 4, 5, 6, 7);
+  };
+
   // ---- S^T = K_j Q_i^T (fp32 accumulation of exact bf16 products)
+  const f32x16 zero = {};
   f32x16 s[C::SB];
-#pragma unroll
-  for (int sb = 0; sb < C::SB; ++sb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[sb][i] = 0.f;
-  const int ksw = swz(l32);
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
-    for (int sb = 0; sb < C::SB; ++sb) {
-      const int row = sb * 32 + l32;
-      const bf16x8 a = *(const bf16x8 LDS_AS*)(kt + row * C::ROWB + 16 * ((2 * kb + h) ^ ksw));
-      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[kb], s[sb], 0, 0, 0);
-    }
+    for (int sb = 0; sb < C::SB; ++sb)
+      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_k(kb, sb), qr[kb], kb == 0 ? zero : s[sb], 0, 0, 0);
   }
 
-  // ---- mask: keys past N, and keys after the query when causal
+  // ---- mask: key visible iff key < N and (not causal or key <= query);
+  // register i of block sb holds key k0 + 32*sb + 8*(i/4) + 4h + i%4.
   if (MASK) {
     const int query = qw0 + l32;
+    const int lim = (CAUSAL ? min(query, N - 1) : N - 1) - (k0 + 4 * h);
 #pragma unroll
     for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + sb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        const bool vis = key < N && (!CAUSAL || key <= query);
-        s[sb][i] = vis ? s[sb][i] : -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i)
+        s[sb][i] = (32 * sb + 8 * (i >> 2) + (i & 3) <= lim) ? s[sb][i] : -INFINITY;
   }
 
   // ---- row max (in-lane over this half's keys, then across the halves)
@@ -171,32 +224,38 @@ __device__ __forceinline__ void attend_tile(const unsigned char LDS_AS* kt, cons
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
   mx = half_max(mx);
-  const float mxs = (mx == -INFINITY) ? -INFINITY : mx * c;  // c >= 0
-  const float m_new = fmaxf(m, mxs);
-  const float mref = (m_new == -INFINITY) ? 0.f : m_new;      // safe reference
-  const float alpha = __builtin_amdgcn_exp2f(m - mref);       // 0 when m = -inf
+  const float mxs = (mx == -INFINITY) ? -INFINITY : mx * c;  // c > 0
 
-  // ---- P = exp2(S*c - m_ref), row sum from the unrounded values
-  float rs = 0.f;
-#pragma unroll
-  for (int sb = 0; sb < C::SB; ++sb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float p = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c, -mref));
-      if (MASK) p = (s[sb][i] == -INFINITY) ? 0.f : p;
-      rs += p;
-      s[sb][i] = p;
-    }
-  lsum = alpha * lsum + rs;
-
-  // ---- rescale the running output only when some row's max moved
-  if (__builtin_amdgcn_ballot_w64(m_new != m)) {
+  bool jump = false;
+  if (EXACT) {
+    const float m_new = fmaxf(m, mxs);
+    const float mref_new = (m_new == -INFINITY) ? 0.f : m_new;  // safe reference
+    const float alpha = __builtin_amdgcn_exp2f(m - mref_new);    // 0 when m = -inf
+    lsum *= alpha;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    m = m_new;
+  } else {
+    // reference set on the first tile of the row; flag a jump over it
+    jump = (m != -INFINITY) && (mxs > m + kSlack);
+    m = (m == -INFINITY) ? mxs : m;
   }
-  m = m_new;
+  const float mref = (m == -INFINITY) ? 0.f : m;  // safe reference
+
+  // ---- P = exp2(S*c - m_ref); masked scores give exp2(-inf) = 0.  The row
+  // sum is taken from the unrounded values.
+#pragma unroll
+  for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[sb][i] = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c, -mref));
+  float rs = 0.f;
+#pragma unroll
+  for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) rs += s[sb][i];
+  lsum += rs;
 
   // ---- P as the bf16 B operand of O^T += V^T P^T (same registers, in order)
   bf16x8 pb[C::PB];
@@ -204,37 +263,25 @@ __device__ __forceinline__ void attend_tile(const unsigned char LDS_AS* kt, cons
   for (int kb2 = 0; kb2 < C::PB; ++kb2)
 #pragma unroll
     for (int j = 0; j < 8; ++j) pb[kb2][j] = (__bf16)s[kb2 >> 1][8 * (kb2 & 1) + j];
-
-  // ---- V^T operand via LDS transpose loads.  Lane (g = lane/16, r, b):
-  // reads V row (16*kb2 + 4h + r [+8]), dims (32*db + 16*(g%2) + 4b .. +3);
-  // after the transpose, lane l holds V[16*kb2 + 4h + 0..3 (+8)][32*db + l%32].
-  const int vr = 4 * h + ((lane >> 2) & 3);
-  const int vsw = swz(vr);
-  const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
-  for (int kb2 = 0; kb2 < C::PB; ++kb2) {
+  for (int kb2 = 0; kb2 < C::PB; ++kb2)
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      const int dim = 32 * db + vdim;
-      const unsigned char LDS_AS* pa =
-          vt + (16 * kb2 + vr) * C::ROWB + 16 * ((dim >> 3) ^ vsw) + 2 * (dim & 7);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)pa);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(pa + 8 * C::ROWB));
-      const bf16x4 lob = __builtin_bit_cast(bf16x4, lo);
-      const bf16x4 hib = __builtin_bit_cast(bf16x4, hi);
-      const bf16x8 a = __builtin_shufflevector(lob, hib, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb2], acc[db], 0, 0, 0);
-    }
-  }
+    for (int db = 0; db < C::DB; ++db)
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_v(kb2, db), pb[kb2], acc[db], 0, 0, 0);
+  return jump;
 }
 
-template <class C, bool CAUSAL>
-__global__ void __launch_bounds__(C::NW * 64)
+// EXACT = false: the fast kernel over every query tile.  EXACT = true: the
+// recompute kernel, which only redoes the query rows the fast kernel marked
+// (NaN LSE) and is a no-op for tiles without a marked row.
+template <class C, bool CAUSAL, bool EXACT>
+__global__ void __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE)))
 fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
                    int N, int T_r, int units_per_head, int num_units, int per_xcd, float c,
                    unsigned int qsign) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * C::TILEB];
+  __shared__ int wave_marked[C::NW];  // recompute kernel only
   unsigned char LDS_AS* sm = (unsigned char LDS_AS*)smem;
 
   const int lane = threadIdx.x & 63;
@@ -259,6 +306,8 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     tiles[1] = ur;
   }
 
+  int it = 0;  // K/V tiles processed so far: selects the LDS stage
+
   const size_t hoff = (size_t)bh * (size_t)N * C::D;
   const uint16_t* qh = q + hoff;
   const uint16_t* kh = k + hoff;
@@ -282,43 +331,69 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       }
     }
 
+    const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
+    const int nkv = (kv_end + C::BC - 1) / C::BC;
+    // leading tiles that need no mask for any query of the workgroup
+    int nfull = min(nkv, N / C::BC);
+    if (CAUSAL) nfull = min(nfull, (q0 + 1) / C::BC);
+
+    bool mine = false;  // recompute kernel: this lane's row was marked
+    if (EXACT) {
+      // redo this query tile only if one of its rows was marked
+      const int query = qw0 + l32;
+      if (query < N) {
+        const float x = lse[(size_t)bh * N + query];
+        mine = x != x;
+      }
+      if (lane == 0) wave_marked[w] = __builtin_amdgcn_ballot_w64(mine) != 0;
+      __syncthreads();
+      int any = 0;
+#pragma unroll
+      for (int ww = 0; ww < C::NW; ++ww) any |= wave_marked[ww];
+      __syncthreads();  // wave_marked is rewritten for the next tile
+      if (!__builtin_amdgcn_readfirstlane(any)) continue;
+    }
+
     float m = -INFINITY, lsum = 0.f;
     f32x16 acc[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+    bool jumped = false;
 
-    const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
-    const int nkv = (kv_end + C::BC - 1) / C::BC;
-
-    load_kv_tile<C>(sm, kh, vh, 0, N, w, lane);
+    load_kv_tile<C>(sm + (it & 1) * 2 * C::TILEB, kh, vh, 0, N, w, lane);
     wait_vm_all();
     __syncthreads();
-
-    for (int j = 0; j < nkv; ++j) {
+    // One step: prefetch the next tile into the other stage, attend to the
+    // current one, then wait for the copies and synchronise the workgroup.
+    int j = 0;
+    for (; j < nfull; ++j) {
       if (j + 1 < nkv)
-        load_kv_tile<C>(sm + ((j + 1) & 1) * 2 * C::TILEB, kh, vh, (j + 1) * C::BC, N, w, lane);
-      const int k0 = j * C::BC;
-      const unsigned char LDS_AS* kt = sm + (j & 1) * 2 * C::TILEB;
-      const unsigned char LDS_AS* vt = kt + C::TILEB;
-      const bool active = !CAUSAL || k0 <= qw0 + 31;  // some key visible to this wave
-      if (active) {
-        const bool need_mask = (k0 + C::BC > N) || (CAUSAL && k0 + C::BC - 1 > qw0);
-        if (need_mask)
-          attend_tile<C, CAUSAL, true>(kt, vt, qr, acc, m, lsum, k0, qw0, N, c, lane);
-        else
-          attend_tile<C, CAUSAL, false>(kt, vt, qr, acc, m, lsum, k0, qw0, N, c, lane);
-      }
+        load_kv_tile<C>(sm + ((it + 1) & 1) * 2 * C::TILEB, kh, vh, (j + 1) * C::BC, N, w, lane);
+      const unsigned char LDS_AS* kt = sm + (it & 1) * 2 * C::TILEB;
+      jumped |= attend_tile<C, CAUSAL, false, EXACT>(kt, kt + C::TILEB, qr, acc, m, lsum, j * C::BC, qw0, N, c,
+                                                     lane);
       wait_vm_all();
       __syncthreads();
+      ++it;
+    }
+    for (; j < nkv; ++j) {
+      if (j + 1 < nkv)
+        load_kv_tile<C>(sm + ((it + 1) & 1) * 2 * C::TILEB, kh, vh, (j + 1) * C::BC, N, w, lane);
+      const unsigned char LDS_AS* kt = sm + (it & 1) * 2 * C::TILEB;
+      jumped |= attend_tile<C, CAUSAL, true, EXACT>(kt, kt + C::TILEB, qr, acc, m, lsum, j * C::BC, qw0, N, c,
+                                                    lane);
+      wait_vm_all();
+      __syncthreads();
+      ++it;
     }
 
     // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
     const float lt = half_sum(lsum);
     const float inv = 1.f / lt;
     const int query = qw0 + l32;
-    if (query < N) {
+    if (query < N && (!EXACT || mine)) {  // the recompute kernel stores only marked rows
       uint16_t* orow = o + hoff + (size_t)query * C::D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -329,7 +404,9 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[db][4 * a + e] * inv);
           *(u32x2*)(orow + 32 * db + 8 * a + 4 * h) = __builtin_bit_cast(u32x2, ov);
         }
-      if (h == 0) lse[(size_t)bh * N + query] = (m + __log2f(lt)) * kLn2;
+      // a row whose scores jumped past the fixed reference is marked (NaN
+      // LSE) for the recompute kernel
+      if (h == 0) lse[(size_t)bh * N + query] = jumped ? __builtin_nanf("") : (m + __log2f(lt)) * kLn2;
     }
   }
 }
@@ -442,7 +519,13 @@ void launch_bf16(const void* q, const void* k, const void* v, void* o, float* ls
   const int num_units = B * H * units_per_head;
   const int per_xcd = (num_units + 7) / 8;
   const int grid = per_xcd * 8;
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL>), dim3(grid), dim3(C::NW * 64), 0, stream,
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, false>), dim3(grid), dim3(C::NW * 64), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, T_r,
+                     units_per_head, num_units, per_xcd, c, qsign);
+  // Waves marked by the fast kernel are redone with exact rescaling; the
+  // launch is ordered after the fast kernel on the stream and its
+  // workgroups exit at once when nothing is marked.
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, true>), dim3(grid), dim3(C::NW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, T_r,
                      units_per_head, num_units, per_xcd, c, qsign);
 }
@@ -454,8 +537,26 @@ void launch_f32(const float* q, const float* k, const float* v, float* o, float*
   hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, stream, q, k, v, o, lse, N, c);
 }
 
-using CfgD128 = Cfg<128, 4, 64>;
-using CfgD64 = Cfg<64, 4, 64>;
+#ifndef FA_D128_NW
+#define FA_D128_NW 8
+#endif
+#ifndef FA_D128_BC
+#define FA_D128_BC 64
+#endif
+#ifndef FA_D128_WPE
+#define FA_D128_WPE 2
+#endif
+#ifndef FA_D64_NW
+#define FA_D64_NW 4
+#endif
+#ifndef FA_D64_BC
+#define FA_D64_BC 64
+#endif
+#ifndef FA_D64_WPE
+#define FA_D64_WPE 2
+#endif
+using CfgD128 = Cfg<128, FA_D128_NW, FA_D128_BC, FA_D128_WPE>;
+using CfgD64 = Cfg<64, FA_D64_NW, FA_D64_BC, FA_D64_WPE>;
 
 }  // namespace
 
@@ -474,7 +575,10 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   // Scores are formed as |scale| * (sign(scale) Q) K^T: a negative scale flips
   // the sign bit of every Q element (exact), so the kernel sees c >= 0.
   const unsigned qsign = (scale < 0.f) ? 0x80008000u : 0u;
-  const float c = fabsf(scale) * kLog2e;
+  // A zero scale runs as 2^-100: every visible weight exp2(s * 2^-100 - m)
+  // then rounds to exactly 1 in fp32 (for |s| < 2^75), i.e. the plain mean
+  // of the visible V rows, while masked scores still map to exp2(-inf) = 0.
+  const float c = scale == 0.f ? 0x1p-100f : fabsf(scale) * kLog2e;
   if (d == 128) {
     if (causal) launch_bf16<CfgD128, true>(q, k, v, o, lse, B, H, N, c, qsign, stream);
     else launch_bf16<CfgD128, false>(q, k, v, o, lse, B, H, N, c, qsign, stream);

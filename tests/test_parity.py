@@ -159,3 +159,24 @@ def test_status_codes_through_binding():
     assert fa.fa_fwd(x, x, x, x, lse, 1, 1, 8, 64, 1.0, 0) == fa.FA_ERR_ALIAS
     assert fa.fa_fwd(x, x, x, o, lse, 1, 1, 8, 64, 1.0, 0) == fa.FA_OK
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_score_jump_recompute(d, causal):
+    """Scores that rise far above the first key tile's maximum (here by ~70
+    in log2 units, past the fast kernel's fixed-reference slack) are redone
+    by the exact-rescaling kernel; the result must still match the oracle."""
+    N = 700
+    g = torch.Generator().manual_seed(d + causal)
+    q = torch.ones(1, 2, N, d) + 0.1 * torch.randn(1, 2, N, d, generator=g)
+    k = 0.1 * torch.randn(1, 2, N, d, generator=g)
+    k[:, :, 300:] += 6.0            # score jump of ~48 (natural log units) after key 300
+    k[:, 1, 500:] += 3.0            # and a second jump on head 1
+    v = torch.randn(1, 2, N, d, generator=g)
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    scale = 1.0 / math.sqrt(d) * math.sqrt(d / 64)
+    say("score jump", d, causal)
+    o, lse = run_gpu(q, k, v, causal, scale)
+    o_ref, lse_ref = attention_ref(f64(q), f64(k), f64(v), scale, causal)
+    assert_close(f64(o), f64(lse), o_ref, lse_ref, torch.bfloat16, f"jump d={d} causal={causal}")
