@@ -18,7 +18,7 @@
 // Attention" (tiles above the diagonal are skipped, only diagonal tiles are
 // masked element by element).
 //
-// gfx950 design (one workgroup = NW wave64s, each wave owns 32 query rows):
+// gfx950 design (one workgroup = 8 wave64s, each wave owns 32 query rows):
 //  * The score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16.  In the MFMA accumulator layout a lane then
 //    holds ONE query (lane % 32) and 16 keys per 32-key block, so the row
@@ -29,9 +29,18 @@
 //    read from a row-major V tile in LDS with ds_read_b64_tr_b16, the gfx950
 //    LDS transpose load.
 //  * K and V tiles are copied HBM -> LDS with global_load_lds_dwordx4
-//    (no VGPR staging), double-buffered, with an XOR swizzle of the 16-byte
-//    chunks so that both the K reads (8 rows x 16 B) and the transposed V
-//    reads (4 rows x 32 B) hit distinct LDS banks.
+//    (no VGPR staging) into a ring of four LDS stages, two tiles ahead of
+//    their use, with an XOR swizzle of the 16-byte chunks so that both the
+//    K reads and the transposed V reads hit distinct LDS banks.
+//  * Each step of a wave is a matrix-core phase (S_j = K_j Q^T and
+//    acc += V_{j-1}^T P_{j-1}^T) and a vector-ALU phase (softmax of S_j).
+//    The two waves of a SIMD run one phase apart, so one feeds the matrix
+//    cores while the other computes exponentials.  In the matrix phase
+//    every LDS address is a per-lane offset computed once plus an
+//    immediate, so that phase issues no vector-ALU work at all.
+//  * The exponent reference of a row is fixed after its first key tile
+//    (no rescaling of acc in the loop); rows whose scores later jump too
+//    far above it are redone by a second, exact-rescaling kernel.
 //  * Exponentials are exp2 with log2(e) folded into the scale; m, l and the
 //    output accumulator stay in fp32 registers; O is divided by l once.
 //  * Work units are query tiles (causal: a heavy tile paired with a light
@@ -70,30 +79,40 @@ constexpr float kLn2 = 0.6931471805599453f;
 // |V| < 2^49; since O = acc / l and LSE = m + log2 l use one common m, the
 // result equals the running-max recurrence in exact arithmetic (the
 // recurrence holds for any common reference; the running max only bounds
-// the exponents).  A wave whose rows jump further marks its LSE rows with
-// NaN and is recomputed by the exact-rescaling kernel.
+// the exponents).  A row whose scores jump further is marked (NaN LSE) and
+// recomputed by the exact-rescaling kernel.
 constexpr float kSlack = 48.0f;
 
 // ---------------------------------------------------------------------------
-// Tile configuration of the bf16 kernel.
-template <int D_, int NW_, int BC_, int WPE_>
+// Tile configuration of the bf16 kernel: 8 waves of 32 query rows each
+// (two waves per SIMD), key tiles of BC rows, a ring of NST LDS stages.
+// LDS layout: the K tiles of the NST stages, then the V tiles.
+template <int D_, int BC_>
 struct Cfg {
   static constexpr int D = D_;             // head dimension
-  static constexpr int NW = NW_;           // waves per workgroup
   static constexpr int BC = BC_;           // keys per K/V tile (B_c)
-  static constexpr int WPE = WPE_;         // waves per SIMD the register budget is sized for
+  static constexpr int NW = 8;             // waves per workgroup
   static constexpr int BR = 32 * NW;       // query rows per tile (B_r)
   static constexpr int ROWB = D * 2;       // bytes of one K/V row
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;     // rows per 1 KB wave-wide copy
-  static constexpr int TILEB = BC * ROWB;  // bytes of one K (or V) tile
-  static constexpr int NINST = TILEB / 1024;
+  static constexpr int KT = BC * ROWB;     // bytes of one K (or V) tile
+  static constexpr int NST = 4;            // LDS stages of the K/V ring
+  static constexpr int VBASE = NST * KT;   // start of the V tiles in LDS
+  static constexpr int LDSB = 2 * NST * KT;
+  static constexpr int NINST = KT / 1024;  // 1 KB copies per matrix per tile
+  static constexpr int NI = NINST / NW;    // ... issued by each wave
+  static constexpr int NCOPY = 2 * NI;     // copy instructions per wave per tile
   static constexpr int KB = D / 16;        // 16-deep k-steps of Q K^T
   static constexpr int DB = D / 32;        // 32-dim output blocks
   static constexpr int SB = BC / 32;       // 32-key score blocks
   static constexpr int PB = BC / 16;       // 16-key k-steps of P V
-  static_assert(NINST % NW == 0, "copy instructions must split evenly over waves");
+  static_assert(NINST % NW == 0 && NI >= 1, "copy instructions must split evenly over waves");
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+  // stage offsets are folded into the 16-bit offset field of the LDS reads
+  static_assert((NST - 1) * KT + (SB - 1) * 32 * ROWB < 65536, "K read offset range");
+  static_assert((NST - 1) * KT + (PB - 1) * 16 * ROWB < 65536, "V read offset range");
+  static_assert(LDSB <= 160 * 1024, "LDS size");
 };
 
 // XOR swizzle of the 16-byte chunk index within a K/V row: chunk c of row r
@@ -106,19 +125,10 @@ struct Cfg {
 // positions, and the 4 rows need distinct values in bits 2-3.  d = 64 (two
 // rows per 256 bytes): rows of equal parity need 8 distinct positions, and
 // rows r, r+2 of a 4-row group must differ in bit 2.
-#ifndef FA_SWZ
-#define FA_SWZ 1
-#endif
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-#if FA_SWZ == 0
-  return ((r & 3) << 1) | ((r >> 2) & 1);
-#elif FA_SWZ == 1
   if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-#else
-  return 0;
-#endif
 }
 
 // Symmetric reductions across the two 32-lane halves (lane l and l ^ 32):
@@ -132,81 +142,214 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-__device__ __forceinline__ void wait_vm_all() {
-  // s_waitcnt vmcnt(0): all vector-memory operations of this wave done,
-  // including the global -> LDS copies.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+// Global -> LDS copies (global_load_lds_dwordx4): lane i writes LDS bytes
+// [m0 + 16 i, m0 + 16 i + 16).  Issued through inline assembly so that the
+// compiler does not make every later LDS read wait for them; the kernel
+// waits for its copies itself (wait_copies) before the barrier that
+// publishes them.  M0 is saved and restored around each copy.
+//  lds_copy16: per-lane 64-bit source address.
+//  lds_copy16_s: wave-uniform 64-bit base (SGPRs) + per-lane 32-bit offset.
+__device__ __forceinline__ void lds_copy16(const void* src, unsigned lds_dst) {
+  const unsigned base = __builtin_amdgcn_readfirstlane(lds_dst);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
+}
+__device__ __forceinline__ void lds_copy16_s(const void* sbase, unsigned voff, unsigned lds_dst) {
+  const unsigned base = __builtin_amdgcn_readfirstlane(lds_dst);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(base)
+      : "memory");
 }
 
-// Issue the HBM -> LDS copies of one K and one V tile (keys k0 .. k0+BC-1).
-// Rows past the end of the sequence are clamped to row N-1: they are never
-// read from HBM past the array, hold finite values, and are masked to -inf
-// (K) / multiplied by an exact 0 (V).
+// s_waitcnt vmcnt(n): at most n vector-memory operations of this wave still
+// outstanding (they complete in order, so every older one has finished).
+template <int n>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier that does not wait for outstanding global -> LDS copies
+// (those are waited for explicitly): LDS accesses of this wave are complete
+// and no memory access moves across it.  The scheduling barriers keep every
+// instruction on its side, so the phases of the kernel loop stay as written.
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Keep the computation of x on this side of the next phase barrier (the
+// compiler would otherwise sink it to its first use in a later phase).
+__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void pin(bf16x8 x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void pin(f32x16 x) { asm volatile("" ::"v"(x)); }
+
+// Per-lane LDS and copy offsets, computed once per workgroup.
 template <class C>
-__device__ __forceinline__ void load_kv_tile(unsigned char LDS_AS* dst, const uint16_t* kh,
-                                             const uint16_t* vh, int k0, int N, int w, int lane) {
+struct LaneOffsets {
+  int k[C::KB];        // K operand of k-step kb: row l%32, dims 16kb + 8(l/32) .. +7
+  int v[C::DB][2];     // V^T operand of output block db, rows +0 / +8 (see tile_m)
+  unsigned g[C::NI];   // this wave's copy instructions: byte offset within a tile
+  int grow[C::NI];     // ... and the tile row they copy
+  int gchunk[C::NI];   // ... and its 16-byte chunk in global memory
+  unsigned base;       // LDS address of the K/V ring
+};
+
+template <class C>
+__device__ __forceinline__ void lane_offsets(LaneOffsets<C>& lo, unsigned base, int w, int lane) {
+  lo.base = base;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int kf = swz<C::D>(l32);
 #pragma unroll
-  for (int ii = 0; ii < C::NINST / C::NW; ++ii) {
-    const int t = w * (C::NINST / C::NW) + ii;
+  for (int kb = 0; kb < C::KB; ++kb) lo.k[kb] = (int)base + l32 * C::ROWB + 16 * ((2 * kb + h) ^ kf);
+  // V^T via LDS transpose loads: lane (g = l/16, r, b) reads V row (16*kb2 +
+  // 4h + r [+8]), dims (32*db + 16*(g%2) + 4b .. +3); after the transpose,
+  // lane l holds V[16*kb2 + 4h + 0..3 (+8)][32*db + l%32].
+  const int vr = 4 * h + ((lane >> 2) & 3);
+  const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int vf0 = swz<C::D>(vr), vf1 = swz<C::D>(vr + 8);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    const int dim = 32 * db + vdim;
+    lo.v[db][0] = (int)base + C::VBASE + vr * C::ROWB + 16 * ((dim >> 3) ^ vf0) + 2 * (dim & 7);
+    lo.v[db][1] = (int)base + C::VBASE + (vr + 8) * C::ROWB + 16 * ((dim >> 3) ^ vf1) + 2 * (dim & 7);
+  }
+#pragma unroll
+  for (int ii = 0; ii < C::NI; ++ii) {
+    const int t = w * C::NI + ii;
     const int row = t * C::RPI + lane / C::CPR;
     const int chunk = (lane % C::CPR) ^ swz<C::D>(row);
-    const int grow = min(k0 + row, N - 1);
-    const size_t off = (size_t)grow * C::D + (size_t)chunk * 8;
-    __builtin_amdgcn_global_load_lds((const void*)(kh + off), (void LDS_AS*)(dst + t * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(vh + off),
-                                     (void LDS_AS*)(dst + C::TILEB + t * 1024), 16, 0, 0);
+    lo.grow[ii] = row;
+    lo.gchunk[ii] = chunk;
+    lo.g[ii] = (unsigned)(row * C::ROWB + chunk * 16);
   }
 }
 
-// One K/V tile for one wave: S^T = K Q^T, online softmax, acc += V^T P^T.
-// MASK: the tile may hold keys past N or, when causal, keys after some
-// query of the wave (masked to -inf, i.e. weight exactly 0).
+// Issue this wave's HBM -> LDS copies of K/V tile k0 .. k0+BC-1 into the
+// stage at byte offset st.  Full tiles use a scalar base and the fixed lane
+// offsets; the last tile of a sequence whose length is not a multiple of BC
+// clamps rows past the end to row N-1 (never read past the array, finite,
+// masked to -inf in K and multiplied by an exact 0 in V).
+template <class C>
+__device__ __forceinline__ void load_kv_tile(int st, const uint16_t* kh, const uint16_t* vh, int k0, int N,
+                                             const LaneOffsets<C>& lo, int w) {
+  if (k0 + C::BC <= N) {
+    const char* kb = (const char*)kh + (size_t)k0 * C::ROWB;
+    const char* vb = (const char*)vh + (size_t)k0 * C::ROWB;
+#pragma unroll
+    for (int ii = 0; ii < C::NI; ++ii) {
+      const unsigned t = (unsigned)(w * C::NI + ii);
+      lds_copy16_s(kb, lo.g[ii], lo.base + st + t * 1024);
+      lds_copy16_s(vb, lo.g[ii], lo.base + C::VBASE + st + t * 1024);
+    }
+  } else {
+#pragma unroll
+    for (int ii = 0; ii < C::NI; ++ii) {
+      const unsigned t = (unsigned)(w * C::NI + ii);
+      const int grow = min(k0 + lo.grow[ii], N - 1);
+      const size_t off = (size_t)grow * C::D + (size_t)lo.gchunk[ii] * 8;
+      lds_copy16(kh + off, lo.base + st + t * 1024);
+      lds_copy16(vh + off, lo.base + C::VBASE + st + t * 1024);
+    }
+  }
+}
+
+// The matrix-core phase of one step: S = K Q^T (HAS_QK, K tile at stage
+// offset kst) and acc += V^T P^T (HAS_PV, V tile at stage offset vst).
+// LDS operands are read a few MFMAs ahead of their use (two k-steps for K,
+// four operands for V), and scheduling barriers keep that order, so that
+// the LDS latency hides behind the matrix cores.  With kst / vst known at
+// compile time, every LDS address is a precomputed lane offset plus an
+// immediate: this phase issues no vector-ALU instruction.
+template <class C, bool HAS_QK, bool HAS_PV>
+__device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& lo, const bf16x8 (&qr)[C::KB],
+                                       f32x16 (&s)[C::SB], const bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB]) {
+  const unsigned char LDS_AS* lds = (const unsigned char LDS_AS*)0;
+  auto load_k = [&](int kb, int sb) -> bf16x8 {
+    return *(const bf16x8 LDS_AS*)(lds + lo.k[kb] + (kst + sb * 32 * C::ROWB));
+  };
+  constexpr int NV = C::PB * C::DB;  // V operands (one per P V instruction)
+  auto load_v = [&](int i) -> bf16x8 {
+    const int kb2 = i / C::DB, db = i % C::DB;
+    const int off = vst + kb2 * 16 * C::ROWB;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + lo.v[db][0] + off));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + lo.v[db][1] + off));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b), 0, 1, 2, 3, 4, 5,
+                                   6, 7);
+  };
+  constexpr int KD = 2;  // K prefetch distance in k-steps
+  constexpr int VD = 4;  // V prefetch distance in operands
+  bf16x8 ka[C::KB][C::SB];
+  bf16x8 va[NV];
+  const f32x16 zero = {};
+  if (HAS_QK) {
+#pragma unroll
+    for (int kb = 0; kb < KD && kb < C::KB; ++kb)
+#pragma unroll
+      for (int sb = 0; sb < C::SB; ++sb) ka[kb][sb] = load_k(kb, sb);
+  } else if (HAS_PV) {
+#pragma unroll
+    for (int i = 0; i < VD && i < NV; ++i) va[i] = load_v(i);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (HAS_QK) {
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+      for (int sb = 0; sb < C::SB; ++sb)
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][sb], qr[kb], kb == 0 ? zero : s[sb], 0, 0, 0);
+      if (kb + KD < C::KB) {
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb) ka[kb + KD][sb] = load_k(kb + KD, sb);
+      } else if (HAS_PV) {
+        // the last k-steps start the V reads
+        const int i0 = (kb + KD - C::KB) * VD / KD, i1 = (kb + KD - C::KB + 1) * VD / KD;
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (i >= i0 && i < i1) va[i] = load_v(i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (HAS_PV) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      acc[i % C::DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb[i / C::DB], acc[i % C::DB], 0, 0, 0);
+      if (i + VD < NV) va[i + VD] = load_v(i + VD);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// The vector-ALU phase: online softmax of one tile.  Mask (MASK: keys past
+// N, and keys after the query when causal, get -inf, i.e. weight exactly
+// 0), row max, exponent reference, P = exp2(S*c - m_ref) into the bf16
+// operand pb, row sum of the unrounded weights into lsum.
 // EXACT = false (fast kernel): fixed reference, no rescaling; returns true
 // in the lanes of a row whose score exceeds its reference by more than
 // kSlack.  EXACT = true (recompute kernel): m is the running max and l and
 // acc are rescaled by exp2(m_old - m_new) on every tile.
 template <class C, bool CAUSAL, bool MASK, bool EXACT>
-__device__ __forceinline__ bool attend_tile(const unsigned char LDS_AS* kt, const unsigned char LDS_AS* vt,
-                                            const bf16x8 (&qr)[C::KB], f32x16 (&acc)[C::DB], float& m,
-                                            float& lsum, int k0, int qw0, int N, float c, int lane) {
+__device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB],
+                                             float& m, float& lsum, int k0, int qw0, int N, float c, int lane) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
-
-  // ---- K operand: lane reads row (32*sb + l%32), dims 16*kb + 8*(l/32) .. +7
-  const unsigned char LDS_AS* krow = kt + l32 * C::ROWB;
-  const int kf = swz<C::D>(l32);
-  auto load_k = [&](int kb, int sb) -> bf16x8 {
-    return *(const bf16x8 LDS_AS*)(krow + sb * 32 * C::ROWB + 16 * ((2 * kb + h) ^ kf));
-  };
-  // ---- V^T operand via LDS transpose loads.  Lane (g = l/16, r, b) reads V
-  // row (16*kb2 + 4h + r [+8]), dims (32*db + 16*(g%2) + 4b .. +3); after
-  // the transpose, lane l holds V[16*kb2 + 4h + 0..3 (+8)][32*db + l%32].
-  const int vr = 4 * h + ((lane >> 2) & 3);
-  const int vdim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int vf0 = swz<C::D>(vr), vf1 = swz<C::D>(vr + 8);
-  auto load_v = [&](int kb2, int db) -> bf16x8 {
-    const int dim = 32 * db + vdim;
-    const unsigned char LDS_AS* base = vt + (16 * kb2 + vr) * C::ROWB + 2 * (dim & 7);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (i16x4 LDS_AS*)(base + 16 * ((dim >> 3) ^ vf0)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (i16x4 LDS_AS*)(base + 8 * C::ROWB + 16 * ((dim >> 3) ^ vf1)));
-    return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi), 0, 1, 2,
-                                   3, 4, 5, 6, 7);
-  };
-
-  // ---- S^T = K_j Q_i^T (fp32 accumulation of exact bf16 products)
-  const f32x16 zero = {};
-  f32x16 s[C::SB];
-#pragma unroll
-  for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-    for (int sb = 0; sb < C::SB; ++sb)
-      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_k(kb, sb), qr[kb], kb == 0 ? zero : s[sb], 0, 0, 0);
-  }
-
-  // ---- mask: key visible iff key < N and (not causal or key <= query);
-  // register i of block sb holds key k0 + 32*sb + 8*(i/4) + 4h + i%4.
+  // register i of block sb holds key k0 + 32*sb + 8*(i/4) + 4h + i%4
   if (MASK) {
     const int query = qw0 + l32;
     const int lim = (CAUSAL ? min(query, N - 1) : N - 1) - (k0 + 4 * h);
@@ -216,14 +359,16 @@ __device__ __forceinline__ bool attend_tile(const unsigned char LDS_AS* kt, cons
       for (int i = 0; i < 16; ++i)
         s[sb][i] = (32 * sb + 8 * (i >> 2) + (i & 3) <= lim) ? s[sb][i] : -INFINITY;
   }
-
-  // ---- row max (in-lane over this half's keys, then across the halves)
-  float mx = -INFINITY;
+  // row max: four independent max chains over this half's keys, then the
+  // two halves of the wave
+  float mq[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) mq[r] = -INFINITY;
 #pragma unroll
   for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
-  mx = half_max(mx);
+    for (int i = 0; i < 16; ++i) mq[i & 3] = fmaxf(mq[i & 3], s[sb][i]);
+  const float mx = half_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
   const float mxs = (mx == -INFINITY) ? -INFINITY : mx * c;  // c > 0
 
   bool jump = false;
@@ -244,30 +389,27 @@ __device__ __forceinline__ bool attend_tile(const unsigned char LDS_AS* kt, cons
   }
   const float mref = (m == -INFINITY) ? 0.f : m;  // safe reference
 
-  // ---- P = exp2(S*c - m_ref); masked scores give exp2(-inf) = 0.  The row
-  // sum is taken from the unrounded values.
+  // P = exp2(S*c - m_ref); masked scores give exp2(-inf) = 0
+  float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[sb][i] = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c, -mref));
-  float rs = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      s[sb][i] = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c, -mref));
+      sq[i & 3] += s[sb][i];
+    }
+  lsum += (sq[0] + sq[1]) + (sq[2] + sq[3]);
 #pragma unroll
-  for (int sb = 0; sb < C::SB; ++sb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) rs += s[sb][i];
-  lsum += rs;
-
-  // ---- P as the bf16 B operand of O^T += V^T P^T (same registers, in order)
-  bf16x8 pb[C::PB];
-#pragma unroll
-  for (int kb2 = 0; kb2 < C::PB; ++kb2)
+  for (int kb2 = 0; kb2 < C::PB; ++kb2) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) pb[kb2][j] = (__bf16)s[kb2 >> 1][8 * (kb2 & 1) + j];
+    pin(pb[kb2]);
+  }
+  pin(lsum);
+  if (EXACT) {
 #pragma unroll
-  for (int kb2 = 0; kb2 < C::PB; ++kb2)
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_v(kb2, db), pb[kb2], acc[db], 0, 0, 0);
+    for (int db = 0; db < C::DB; ++db) pin(acc[db]);
+  }
   return jump;
 }
 
@@ -275,14 +417,14 @@ __device__ __forceinline__ bool attend_tile(const unsigned char LDS_AS* kt, cons
 // recompute kernel, which only redoes the query rows the fast kernel marked
 // (NaN LSE) and is a no-op for tiles without a marked row.
 template <class C, bool CAUSAL, bool EXACT>
-__global__ void __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(C::WPE, C::WPE)))
+__global__ void __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
                    int N, int T_r, int units_per_head, int num_units, int per_xcd, float c,
                    unsigned int qsign) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * C::TILEB];
-  __shared__ int wave_marked[C::NW];  // recompute kernel only
-  unsigned char LDS_AS* sm = (unsigned char LDS_AS*)smem;
+  // the K/V ring, then one flag per wave (recompute kernel)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDSB + 4 * C::NW];
+  int LDS_AS* wave_marked = (int LDS_AS*)(smem + C::LDSB);
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -306,7 +448,8 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     tiles[1] = ur;
   }
 
-  int it = 0;  // K/V tiles processed so far: selects the LDS stage
+  LaneOffsets<C> lo;
+  lane_offsets<C>(lo, (unsigned)(uintptr_t)(const unsigned char LDS_AS*)smem, w, lane);
 
   const size_t hoff = (size_t)bh * (size_t)N * C::D;
   const uint16_t* qh = q + hoff;
@@ -316,6 +459,22 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   for (int ti = 0; ti < ntiles; ++ti) {
     const int q0 = tiles[ti] * C::BR;
     const int qw0 = q0 + w * 32;
+
+    bool mine = false;  // recompute kernel: this lane's row was marked
+    if (EXACT) {
+      const int query = qw0 + l32;
+      if (query < N) {
+        const float x = lse[(size_t)bh * N + query];
+        mine = x != x;
+      }
+      if (lane == 0) wave_marked[w] = __builtin_amdgcn_ballot_w64(mine) != 0;
+      __syncthreads();
+      int any = 0;
+#pragma unroll
+      for (int ww = 0; ww < C::NW; ++ww) any |= wave_marked[ww];
+      __syncthreads();  // wave_marked is rewritten for the next tile
+      if (!__builtin_amdgcn_readfirstlane(any)) continue;
+    }
 
     // Q_i rows as the B operand of S^T = K Q^T: lane holds query qw0 + l%32,
     // dims 16*kb + 8*(l/32) .. +7.  Rows past N are clamped (never stored).
@@ -337,23 +496,6 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     int nfull = min(nkv, N / C::BC);
     if (CAUSAL) nfull = min(nfull, (q0 + 1) / C::BC);
 
-    bool mine = false;  // recompute kernel: this lane's row was marked
-    if (EXACT) {
-      // redo this query tile only if one of its rows was marked
-      const int query = qw0 + l32;
-      if (query < N) {
-        const float x = lse[(size_t)bh * N + query];
-        mine = x != x;
-      }
-      if (lane == 0) wave_marked[w] = __builtin_amdgcn_ballot_w64(mine) != 0;
-      __syncthreads();
-      int any = 0;
-#pragma unroll
-      for (int ww = 0; ww < C::NW; ++ww) any |= wave_marked[ww];
-      __syncthreads();  // wave_marked is rewritten for the next tile
-      if (!__builtin_amdgcn_readfirstlane(any)) continue;
-    }
-
     float m = -INFINITY, lsum = 0.f;
     f32x16 acc[C::DB];
 #pragma unroll
@@ -362,32 +504,78 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
     bool jumped = false;
 
-    load_kv_tile<C>(sm + (it & 1) * 2 * C::TILEB, kh, vh, 0, N, w, lane);
-    wait_vm_all();
-    __syncthreads();
-    // One step: prefetch the next tile into the other stage, attend to the
-    // current one, then wait for the copies and synchronise the workgroup.
-    int j = 0;
-    for (; j < nfull; ++j) {
-      if (j + 1 < nkv)
-        load_kv_tile<C>(sm + ((it + 1) & 1) * 2 * C::TILEB, kh, vh, (j + 1) * C::BC, N, w, lane);
-      const unsigned char LDS_AS* kt = sm + (it & 1) * 2 * C::TILEB;
-      jumped |= attend_tile<C, CAUSAL, false, EXACT>(kt, kt + C::TILEB, qr, acc, m, lsum, j * C::BC, qw0, N, c,
-                                                     lane);
-      wait_vm_all();
-      __syncthreads();
-      ++it;
+    // Phases.  Each step j of a wave is a matrix-core phase M(j) -- issue
+    // this wave's copies of tile j+2, S_j = K_j Q^T, acc += V_{j-1}^T
+    // P_{j-1}^T -- followed by a vector-ALU phase V(j) -- the softmax of S_j
+    // into P_j -- with a workgroup barrier after every phase.  Waves w and
+    // w + 4 share a SIMD; waves 4..7 run one phase behind waves 0..3 (one
+    // extra barrier at the start, one fewer at the end), so on every SIMD
+    // one wave feeds the matrix cores while the other computes
+    // exponentials.  K/V tiles rotate through NST = 4 LDS stages (tile t in
+    // stage t % 4); a tile's copies are issued two steps ahead and waited
+    // for at the end of the M phase before the one that reads it, and its
+    // stage is refilled (with tile t+4) only after the lagging half's P V
+    // of tile t.
+    const bool lag = w >= C::NW / 2;
+    f32x16 s[C::SB];
+    bf16x8 p[C::PB];  // P_{j-1} is read in M(j), then P_j is written in V(j)
+    auto end_m = [&](int j) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) pin(acc[db]);
+#pragma unroll
+      for (int sb = 0; sb < C::SB; ++sb) pin(s[sb]);
+      // the copies of tile j+1 (issued one step earlier) have landed; those
+      // of tile j+2 (issued in this phase) may still be in flight
+      if (j + 2 < nkv) wait_copies<C::NCOPY>();
+      else wait_copies<0>();
+      barrier();
+    };
+    auto softmax = [&](int j, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      jumped |= tile_softmax<C, CAUSAL, MASK, EXACT>(s, p, acc, m, lsum, j * C::BC, qw0, N, c, lane);
+      barrier();
+    };
+    // one step with the stages of tiles j, j-1, j+2 given (compile-time
+    // constants in the unrolled loop, run-time values otherwise)
+    auto step = [&](int j, int kst, int vst, int dst, auto mask_tag) {
+      if (j + 2 < nkv) load_kv_tile<C>(dst, kh, vh, (j + 2) * C::BC, N, lo, w);
+      tile_m<C, true, true>(kst, vst, lo, qr, s, p, acc);
+      end_m(j);
+      softmax(j, mask_tag);
+    };
+
+    load_kv_tile<C>(0, kh, vh, 0, N, lo, w);
+    if (1 < nkv) load_kv_tile<C>(C::KT, kh, vh, C::BC, N, lo, w);
+    wait_copies<0>();
+    barrier();
+    if (lag) barrier();
+    // M(0), V(0)
+    if (2 < nkv) load_kv_tile<C>(2 * C::KT, kh, vh, 2 * C::BC, N, lo, w);
+    tile_m<C, true, false>(0, 0, lo, qr, s, p, acc);
+    end_m(0);
+    if (nfull > 0) softmax(0, std::false_type{});
+    else softmax(0, std::true_type{});
+    // unmasked steps 1 .. j1-1, unrolled by the ring size so that every
+    // stage offset is a compile-time constant (step j uses stage j % 4)
+    const int j1 = max(1, min(nfull, nkv));
+    int j = 1;
+    constexpr int KT = C::KT;
+    for (; j + 3 < j1; j += 4) {
+      step(j + 0, 1 * KT, 0 * KT, 3 * KT, std::false_type{});
+      step(j + 1, 2 * KT, 1 * KT, 0 * KT, std::false_type{});
+      step(j + 2, 3 * KT, 2 * KT, 1 * KT, std::false_type{});
+      step(j + 3, 0 * KT, 3 * KT, 2 * KT, std::false_type{});
     }
-    for (; j < nkv; ++j) {
-      if (j + 1 < nkv)
-        load_kv_tile<C>(sm + ((it + 1) & 1) * 2 * C::TILEB, kh, vh, (j + 1) * C::BC, N, w, lane);
-      const unsigned char LDS_AS* kt = sm + (it & 1) * 2 * C::TILEB;
-      jumped |= attend_tile<C, CAUSAL, true, EXACT>(kt, kt + C::TILEB, qr, acc, m, lsum, j * C::BC, qw0, N, c,
-                                                    lane);
-      wait_vm_all();
-      __syncthreads();
-      ++it;
-    }
+    if (j < j1) { step(j, 1 * KT, 0 * KT, 3 * KT, std::false_type{}); ++j; }
+    if (j < j1) { step(j, 2 * KT, 1 * KT, 0 * KT, std::false_type{}); ++j; }
+    if (j < j1) { step(j, 3 * KT, 2 * KT, 1 * KT, std::false_type{}); ++j; }
+    // remaining (masked) steps, stages at run time
+    for (; j < nkv; ++j)
+      step(j, (j & 3) * KT, ((j - 1) & 3) * KT, ((j + 2) & 3) * KT, std::true_type{});
+    // M(nkv): the last P V
+    tile_m<C, false, true>(0, ((nkv - 1) & 3) * KT, lo, qr, s, p, acc);
+    if (!lag) barrier();
+    barrier();  // every wave is done with the LDS ring before it is refilled
 
     // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
     const float lt = half_sum(lsum);
@@ -537,26 +725,14 @@ void launch_f32(const float* q, const float* k, const float* v, float* o, float*
   hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, stream, q, k, v, o, lse, N, c);
 }
 
-#ifndef FA_D128_NW
-#define FA_D128_NW 8
-#endif
 #ifndef FA_D128_BC
 #define FA_D128_BC 64
 #endif
-#ifndef FA_D128_WPE
-#define FA_D128_WPE 2
-#endif
-#ifndef FA_D64_NW
-#define FA_D64_NW 4
-#endif
 #ifndef FA_D64_BC
-#define FA_D64_BC 64
+#define FA_D64_BC 128
 #endif
-#ifndef FA_D64_WPE
-#define FA_D64_WPE 2
-#endif
-using CfgD128 = Cfg<128, FA_D128_NW, FA_D128_BC, FA_D128_WPE>;
-using CfgD64 = Cfg<64, FA_D64_NW, FA_D64_BC, FA_D64_WPE>;
+using CfgD128 = Cfg<128, FA_D128_BC>;
+using CfgD64 = Cfg<64, FA_D64_BC>;
 
 }  // namespace
 
