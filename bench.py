@@ -9,7 +9,9 @@ causal, with Q/K/V already resident in HBM.  Prints ONE JSON line:
                           FLOPs halved for causal, over the timed steps
   roofline                the kernel against the bf16 dense matrix-core peak
                           (achieved = FLOPs per launch / average launch time
-                          from HIP events on the launch stream)
+                          from HIP events on the launch stream; traffic = HBM
+                          bytes per launch from the committed profiler
+                          counters, null if the kernel source changed since)
   cpu_baseline            the fp64 CPU oracle timed on a bounded sample of
                           the same workload on this host's cores
 
@@ -17,6 +19,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -29,6 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak (2.5 PFLOP/s)
 DEFAULT_WORKLOAD = "longctx_n16384_d128_causal"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "io_aware_exact_fa1_amd", "csrc", "fa_fwd.hip")
 
 
 def log(*a):
@@ -63,6 +67,23 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     log(f"[copy-cal] copied {n} bytes x5")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed profiler counters
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading), or
+    None when they were taken on another workload or on a kernel source
+    other than the one built here."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("kernel_source_sha256") != sha:
+        return None
+    return t.get("bytes_per_launch")
 
 
 def cpu_baseline(w, q, k, v, target_s):
@@ -180,15 +201,7 @@ def main():
         f"(median {med_ms:.3f}, min {launch_ms[0]:.3f}) -> {achieved:.1f} TFLOP/s "
         f"= {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 dense peak")
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            with open(TRAFFIC_FILE) as f:
-                t = json.load(f)
-            if t.get("workload") == w.name:
-                traffic = t.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic(w.name)
 
     cpu = None
     if not args.no_cpu_baseline:
