@@ -73,15 +73,17 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Exponent reference of the fast kernel.  Each row's reference m is fixed
-// at the max of its first key tile.  While no later score exceeds it by more
-// than kSlack (log2 units), the unnormalised weights p = exp2(s*c - m) stay
-// <= 2^kSlack, l <= N * 2^kSlack < 2^79 and acc cannot overflow for
-// |V| < 2^49; since O = acc / l and LSE = m + log2 l use one common m, the
-// result equals the running-max recurrence in exact arithmetic (the
-// recurrence holds for any common reference; the running max only bounds
-// the exponents).  A row whose scores jump further is marked (NaN LSE) and
-// recomputed by the exact-rescaling kernel.
+// at the max of its first key tile, and later tiles compute no max.  While
+// the weights p = exp2(s*c - m) that one lane sums per tile stay <= 2^kSlack
+// (so every single weight does), l <= N * 2^kSlack < 2^79 and acc cannot
+// overflow for |V| < 2^49; since O = acc / l and LSE = m + log2 l use one
+// common m, the result equals the running-max recurrence in exact
+// arithmetic (the recurrence holds for any common reference; the running
+// max only bounds the exponents).  A row whose tile sum exceeds the bound
+// (a score jumped more than kSlack above the reference, or overflowed to
+// +inf) is marked (NaN LSE) and recomputed by the exact-rescaling kernel.
 constexpr float kSlack = 48.0f;
+constexpr float kJumpSum = 0x1p48f;  // 2^kSlack
 
 // ---------------------------------------------------------------------------
 // Tile configuration of the bf16 kernel: 8 waves of 32 query rows each
@@ -101,13 +103,21 @@ struct Cfg {
   static constexpr int VBASE = NST * KT;   // start of the V tiles in LDS
   static constexpr int LDSB = 2 * NST * KT;
   static constexpr int NINST = KT / 1024;  // 1 KB copies per matrix per tile
-  static constexpr int NI = NINST / NW;    // ... issued by each wave
-  static constexpr int NCOPY = 2 * NI;     // copy instructions per wave per tile
+  static constexpr int NCW = NW / 2;       // waves copying one matrix (K: waves 0..3, V: 4..7)
+  static constexpr int NI = NINST / NCW;   // copy instructions per wave per tile
   static constexpr int KB = D / 16;        // 16-deep k-steps of Q K^T
   static constexpr int DB = D / 32;        // 32-dim output blocks
   static constexpr int SB = BC / 32;       // 32-key score blocks
   static constexpr int PB = BC / 16;       // 16-key k-steps of P V
-  static_assert(NINST % NW == 0 && NI >= 1, "copy instructions must split evenly over waves");
+  static_assert(NINST % NCW == 0 && NI >= 1, "copy instructions must split evenly over waves");
+  static_assert(NI <= 15, "copies of one tile must fit the wait counter");
+  static constexpr int KD = 2;             // K operands read ahead, in k-steps
+  // Where the global -> LDS copies go: true = in the vector phase, three
+  // tiles ahead (d = 128, where the matrix phase is the longer one); false =
+  // at the start of the matrix phase, two tiles ahead (d = 64, where the
+  // softmax of BC = 128 keys is the longer one).
+  static constexpr bool VCOPY = D == 128;
+  static_assert((NCW * RPI) % 16 == 0, "a wave's copy rows must be a swizzle period apart");
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
   // stage offsets are folded into the 16-bit offset field of the LDS reads
   static_assert((NST - 1) * KT + (SB - 1) * 32 * ROWB < 65536, "K read offset range");
@@ -199,13 +209,17 @@ __device__ __forceinline__ void pin(bf16x8 x) { asm volatile("" ::"v"(x)); }
 __device__ __forceinline__ void pin(f32x16 x) { asm volatile("" ::"v"(x)); }
 
 // Per-lane LDS and copy offsets, computed once per workgroup.
+// Waves 0..NCW-1 copy the K tiles, waves NCW..2NCW-1 the V tiles.  Copy
+// instruction ii of wave w moves the 1 KB block t = w % NCW + NCW * ii of
+// its matrix, i.e. tile rows RPI*t .. RPI*t + RPI-1 (to LDS bytes 1024 t ..);
+// consecutive instructions of a wave are NCW*RPI rows apart, a multiple of
+// the swizzle period, so one lane offset serves them all and the rest is a
+// wave-uniform base.
 template <class C>
 struct LaneOffsets {
   int k[C::KB];        // K operand of k-step kb: row l%32, dims 16kb + 8(l/32) .. +7
   int v[C::DB][2];     // V^T operand of output block db, rows +0 / +8 (see tile_m)
-  unsigned g[C::NI];   // this wave's copy instructions: byte offset within a tile
-  int grow[C::NI];     // ... and the tile row they copy
-  int gchunk[C::NI];   // ... and its 16-byte chunk in global memory
+  unsigned g;          // copies: byte offset of this lane's 16 bytes within block w
   unsigned base;       // LDS address of the K/V ring
 };
 
@@ -229,60 +243,75 @@ __device__ __forceinline__ void lane_offsets(LaneOffsets<C>& lo, unsigned base, 
     lo.v[db][0] = (int)base + C::VBASE + vr * C::ROWB + 16 * ((dim >> 3) ^ vf0) + 2 * (dim & 7);
     lo.v[db][1] = (int)base + C::VBASE + (vr + 8) * C::ROWB + 16 * ((dim >> 3) ^ vf1) + 2 * (dim & 7);
   }
+  const int row = (w % C::NCW) * C::RPI + lane / C::CPR;  // row of block w % NCW
+  const int chunk = (lane % C::CPR) ^ swz<C::D>(row);
+  lo.g = (unsigned)(lane / C::CPR * C::ROWB + chunk * 16);
+}
+
+// This wave's HBM -> LDS copies of its matrix (K for waves 0..NCW-1, V for
+// the others; src is that matrix of the head) for tile k0 .. k0+BC-1, into
+// the stage at byte offset st.  A full tile uses a scalar base and the
+// fixed lane offset; the last tile of a sequence whose length is not a
+// multiple of BC clamps rows past the end to row N-1 (never read past the
+// array, finite, masked to -inf in K and multiplied by an exact 0 in V).
+template <class C>
+__device__ __forceinline__ void load_tile(const uint16_t* src, unsigned lds_st, int k0, int N,
+                                          const LaneOffsets<C>& lo, int w) {
+  const int wc = w % C::NCW;
+  if (k0 + C::BC <= N) {
 #pragma unroll
-  for (int ii = 0; ii < C::NI; ++ii) {
-    const int t = w * C::NI + ii;
-    const int row = t * C::RPI + lane / C::CPR;
-    const int chunk = (lane % C::CPR) ^ swz<C::D>(row);
-    lo.grow[ii] = row;
-    lo.gchunk[ii] = chunk;
-    lo.g[ii] = (unsigned)(row * C::ROWB + chunk * 16);
+    for (int ii = 0; ii < C::NI; ++ii) {
+      const int t = wc + C::NCW * ii;
+      const char* base = (const char*)src + ((size_t)k0 + (size_t)t * C::RPI) * C::ROWB;
+      lds_copy16_s(base, lo.g, lds_st + t * 1024);
+    }
+  } else {
+    // (the lane index is made opaque so that the compiler recomputes these
+    // rarely used addresses here instead of keeping them live in registers)
+    int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(lane));
+#pragma unroll
+    for (int ii = 0; ii < C::NI; ++ii) {
+      const int t = wc + C::NCW * ii;
+      const int row = t * C::RPI + lane / C::CPR;
+      const int chunk = (lane % C::CPR) ^ swz<C::D>(row);
+      const int grow = min(k0 + row, N - 1);
+      lds_copy16(src + (size_t)grow * C::D + (size_t)chunk * 8, lds_st + t * 1024);
+    }
   }
 }
 
-// Issue this wave's HBM -> LDS copies of K/V tile k0 .. k0+BC-1 into the
-// stage at byte offset st.  Full tiles use a scalar base and the fixed lane
-// offsets; the last tile of a sequence whose length is not a multiple of BC
-// clamps rows past the end to row N-1 (never read past the array, finite,
-// masked to -inf in K and multiplied by an exact 0 in V).
+// K operand of k-step kb, 32-key block sb, of the K tile at stage offset kst.
 template <class C>
-__device__ __forceinline__ void load_kv_tile(int st, const uint16_t* kh, const uint16_t* vh, int k0, int N,
-                                             const LaneOffsets<C>& lo, int w) {
-  if (k0 + C::BC <= N) {
-    const char* kb = (const char*)kh + (size_t)k0 * C::ROWB;
-    const char* vb = (const char*)vh + (size_t)k0 * C::ROWB;
+__device__ __forceinline__ bf16x8 lds_k(const LaneOffsets<C>& lo, int kst, int kb, int sb) {
+  const unsigned char LDS_AS* lds = (const unsigned char LDS_AS*)0;
+  return *(const bf16x8 LDS_AS*)(lds + lo.k[kb] + (kst + sb * 32 * C::ROWB));
+}
+
+// The K operands of the first KD k-steps of the tile at stage offset kst,
+// read ahead of the matrix phase that uses them.
+template <class C>
+__device__ __forceinline__ void prefetch_k(bf16x8 (&kpre)[C::KD][C::SB], const LaneOffsets<C>& lo, int kst) {
 #pragma unroll
-    for (int ii = 0; ii < C::NI; ++ii) {
-      const unsigned t = (unsigned)(w * C::NI + ii);
-      lds_copy16_s(kb, lo.g[ii], lo.base + st + t * 1024);
-      lds_copy16_s(vb, lo.g[ii], lo.base + C::VBASE + st + t * 1024);
-    }
-  } else {
+  for (int kb = 0; kb < C::KD; ++kb)
 #pragma unroll
-    for (int ii = 0; ii < C::NI; ++ii) {
-      const unsigned t = (unsigned)(w * C::NI + ii);
-      const int grow = min(k0 + lo.grow[ii], N - 1);
-      const size_t off = (size_t)grow * C::D + (size_t)lo.gchunk[ii] * 8;
-      lds_copy16(kh + off, lo.base + st + t * 1024);
-      lds_copy16(vh + off, lo.base + C::VBASE + st + t * 1024);
-    }
-  }
+    for (int sb = 0; sb < C::SB; ++sb) kpre[kb][sb] = lds_k<C>(lo, kst, kb, sb);
 }
 
 // The matrix-core phase of one step: S = K Q^T (HAS_QK, K tile at stage
 // offset kst) and acc += V^T P^T (HAS_PV, V tile at stage offset vst).
 // LDS operands are read a few MFMAs ahead of their use (two k-steps for K,
 // four operands for V), and scheduling barriers keep that order, so that
-// the LDS latency hides behind the matrix cores.  With kst / vst known at
+// the LDS latency hides behind the matrix cores; the first KD k-steps of K
+// come in kpre, read during the preceding phase.  With kst / vst known at
 // compile time, every LDS address is a precomputed lane offset plus an
-// immediate: this phase issues no vector-ALU instruction.
+// immediate: this phase issues no vector-ALU instruction and no copy.
 template <class C, bool HAS_QK, bool HAS_PV>
 __device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& lo, const bf16x8 (&qr)[C::KB],
-                                       f32x16 (&s)[C::SB], const bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB]) {
+                                       f32x16 (&s)[C::SB], const bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB],
+                                       const bf16x8 (&kpre)[C::KD][C::SB]) {
   const unsigned char LDS_AS* lds = (const unsigned char LDS_AS*)0;
-  auto load_k = [&](int kb, int sb) -> bf16x8 {
-    return *(const bf16x8 LDS_AS*)(lds + lo.k[kb] + (kst + sb * 32 * C::ROWB));
-  };
+  auto load_k = [&](int kb, int sb) -> bf16x8 { return lds_k<C>(lo, kst, kb, sb); };
   constexpr int NV = C::PB * C::DB;  // V operands (one per P V instruction)
   auto load_v = [&](int i) -> bf16x8 {
     const int kb2 = i / C::DB, db = i % C::DB;
@@ -292,8 +321,8 @@ __device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& l
     return __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b), 0, 1, 2, 3, 4, 5,
                                    6, 7);
   };
-  constexpr int KD = 2;  // K prefetch distance in k-steps
-  constexpr int VD = 4;  // V prefetch distance in operands
+  constexpr int KD = C::KD;  // K prefetch distance in k-steps
+  constexpr int VD = 4;      // V prefetch distance in operands
   bf16x8 ka[C::KB][C::SB];
   bf16x8 va[NV];
   const f32x16 zero = {};
@@ -301,7 +330,7 @@ __device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& l
 #pragma unroll
     for (int kb = 0; kb < KD && kb < C::KB; ++kb)
 #pragma unroll
-      for (int sb = 0; sb < C::SB; ++sb) ka[kb][sb] = load_k(kb, sb);
+      for (int sb = 0; sb < C::SB; ++sb) ka[kb][sb] = kpre[kb][sb];
   } else if (HAS_PV) {
 #pragma unroll
     for (int i = 0; i < VD && i < NV; ++i) va[i] = load_v(i);
@@ -338,13 +367,15 @@ __device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& l
 
 // The vector-ALU phase: online softmax of one tile.  Mask (MASK: keys past
 // N, and keys after the query when causal, get -inf, i.e. weight exactly
-// 0), row max, exponent reference, P = exp2(S*c - m_ref) into the bf16
-// operand pb, row sum of the unrounded weights into lsum.
-// EXACT = false (fast kernel): fixed reference, no rescaling; returns true
-// in the lanes of a row whose score exceeds its reference by more than
-// kSlack.  EXACT = true (recompute kernel): m is the running max and l and
-// acc are rescaled by exp2(m_old - m_new) on every tile.
-template <class C, bool CAUSAL, bool MASK, bool EXACT>
+// 0), exponent reference, P = exp2(S*c - m_ref) into the bf16 operand pb,
+// row sum of the unrounded weights into lsum.
+// EXACT = false (fast kernel): the first tile (FIRST) sets the reference to
+// its row max; later tiles compute no max at all and return true in a lane
+// whose weights of this tile sum to more than 2^kSlack (which every weight
+// above 2^kSlack, or an overflow to +inf, implies).
+// EXACT = true (recompute kernel): m is the running max and l and acc are
+// rescaled by exp2(m_old - m_new) on every tile.
+template <class C, bool CAUSAL, bool MASK, bool EXACT, bool FIRST>
 __device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB],
                                              float& m, float& lsum, int k0, int qw0, int N, float c, int lane) {
   const int l32 = lane & 31;
@@ -359,46 +390,48 @@ __device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
       for (int i = 0; i < 16; ++i)
         s[sb][i] = (32 * sb + 8 * (i >> 2) + (i & 3) <= lim) ? s[sb][i] : -INFINITY;
   }
-  // row max: four independent max chains over this half's keys, then the
-  // two halves of the wave
-  float mq[4];
+  if (EXACT || FIRST) {
+    // row max: four independent max chains over this half's keys, then the
+    // two halves of the wave
+    float mq[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) mq[r] = -INFINITY;
+    for (int r = 0; r < 4; ++r) mq[r] = s[0][r];
 #pragma unroll
-  for (int sb = 0; sb < C::SB; ++sb)
+    for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mq[i & 3] = fmaxf(mq[i & 3], s[sb][i]);
-  const float mx = half_max(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
-  const float mxs = (mx == -INFINITY) ? -INFINITY : mx * c;  // c > 0
-
-  bool jump = false;
-  if (EXACT) {
-    const float m_new = fmaxf(m, mxs);
-    const float mref_new = (m_new == -INFINITY) ? 0.f : m_new;  // safe reference
-    const float alpha = __builtin_amdgcn_exp2f(m - mref_new);    // 0 when m = -inf
-    lsum *= alpha;
+      for (int i = (sb == 0 ? 4 : 0); i < 16; ++i) mq[i & 3] = __builtin_fmaxf(mq[i & 3], s[sb][i]);
+    const float mx = half_max(__builtin_fmaxf(__builtin_fmaxf(mq[0], mq[1]), __builtin_fmaxf(mq[2], mq[3])));
+    const float mxs = (mx == -INFINITY) ? -INFINITY : mx * c;  // c > 0
+    if (EXACT) {
+      const float m_new = __builtin_fmaxf(m, mxs);
+      const float mref_new = (m_new == -INFINITY) ? 0.f : m_new;  // safe reference
+      const float alpha = __builtin_amdgcn_exp2f(m - mref_new);    // 0 when m = -inf
+      lsum *= alpha;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-    m = m_new;
-  } else {
-    // reference set on the first tile of the row; flag a jump over it
-    jump = (m != -INFINITY) && (mxs > m + kSlack);
-    m = (m == -INFINITY) ? mxs : m;
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      m = m_new;
+    } else {
+      m = mxs;
+    }
   }
-  const float mref = (m == -INFINITY) ? 0.f : m;  // safe reference
+  // safe reference; after the first tile of the fast kernel m is the finite
+  // max of a tile that holds a visible key of every row (key 0)
+  const float mref = (EXACT || FIRST) ? ((m == -INFINITY) ? 0.f : m) : m;
 
   // P = exp2(S*c - m_ref); masked scores give exp2(-inf) = 0
-  float sq[4] = {0.f, 0.f, 0.f, 0.f};
+  float sq[4];
 #pragma unroll
   for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       s[sb][i] = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c, -mref));
-      sq[i & 3] += s[sb][i];
+      if (sb == 0 && i < 4) sq[i] = s[sb][i];
+      else sq[i & 3] += s[sb][i];
     }
-  lsum += (sq[0] + sq[1]) + (sq[2] + sq[3]);
+  const float ts = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+  lsum += ts;
 #pragma unroll
   for (int kb2 = 0; kb2 < C::PB; ++kb2) {
 #pragma unroll
@@ -410,7 +443,8 @@ __device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) pin(acc[db]);
   }
-  return jump;
+  // NaN-safe: a NaN sum (NaN inputs) is not flagged
+  return !EXACT && !FIRST && ts > kJumpSum;
 }
 
 // EXACT = false: the fast kernel over every query tile.  EXACT = true: the
@@ -504,81 +538,124 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
     bool jumped = false;
 
-    // Phases.  Each step j of a wave is a matrix-core phase M(j) -- issue
-    // this wave's copies of tile j+2, S_j = K_j Q^T, acc += V_{j-1}^T
-    // P_{j-1}^T -- followed by a vector-ALU phase V(j) -- the softmax of S_j
-    // into P_j -- with a workgroup barrier after every phase.  Waves w and
-    // w + 4 share a SIMD; waves 4..7 run one phase behind waves 0..3 (one
-    // extra barrier at the start, one fewer at the end), so on every SIMD
-    // one wave feeds the matrix cores while the other computes
-    // exponentials.  K/V tiles rotate through NST = 4 LDS stages (tile t in
-    // stage t % 4); a tile's copies are issued two steps ahead and waited
-    // for at the end of the M phase before the one that reads it, and its
-    // stage is refilled (with tile t+4) only after the lagging half's P V
-    // of tile t.
-    const bool lag = w >= C::NW / 2;
+    // Phases.  Each step j of a wave is a matrix-core phase M(j) -- S_j =
+    // K_j Q^T and acc += V_{j-1}^T P_{j-1}^T -- followed by a vector-ALU
+    // phase V(j) -- the softmax of S_j into P_j -- with a workgroup barrier
+    // after every phase.  Waves w and w + 4 share a SIMD; waves 4..7 run one
+    // phase behind waves 0..3 (one extra barrier at the start, one fewer at
+    // the end), so on every SIMD one wave feeds the matrix cores while the
+    // other computes exponentials; the matrix phase runs at raised wave
+    // priority so that its MFMAs issue first.
+    // K and V tiles rotate through NST = 4 LDS stages each (tile t in stage
+    // t % 4); waves 0..3 copy K, waves 4..7 copy V.  Number the barriers so
+    // that the leading half's M(j) ends at barrier 2j+2 (the lagging half's
+    // at 2j+3).  K_t is last read in the lagging M(t) (ends 2t+3), V_t in the
+    // lagging M(t+1) (ends 2t+5).
+    //  VCOPY: V(j) also issues this wave's copies for tile j+3, waits for its
+    //   copies of tile j+2, and reads ahead the first K operands of tile
+    //   j+1.  The leading half writes K_{t+4} from barrier 2t+4 on, the
+    //   lagging half V_{t+4} from 2t+5 on: after the last reads of the
+    //   stage; both waits end by barrier 2t+8, before tile t+4 is first read
+    //   (the read-ahead in the leading V(t+3)).
+    //  !VCOPY: M(j) starts with this wave's copies for tile j+2 and ends
+    //   with the wait for its copies of tile j+1.  K_{t+4} is written from
+    //   barrier 2t+5 (leading M(t+2)), V_{t+4} from 2t+6; K_{t+4} has landed
+    //   by 2t+8 (end of the leading M(t+3)) and V_{t+4} by 2t+9, before their
+    //   first reads (leading M(t+4) from 2t+9, and its P V in M(t+5)).
+    constexpr bool VC = C::VCOPY;
+    constexpr int AHEAD = VC ? 3 : 2;  // copies run this many tiles ahead
+    const bool lag = w >= C::NCW;
+    const uint16_t* msrc = lag ? vh : kh;                     // the matrix this wave copies
+    const unsigned mdst = lo.base + (lag ? C::VBASE : 0u);  // ... and its LDS ring
     f32x16 s[C::SB];
     bf16x8 p[C::PB];  // P_{j-1} is read in M(j), then P_j is written in V(j)
-    auto end_m = [&](int j) {
+    bf16x8 kpre[C::KD][C::SB];
+    // M(j) (HAS_QK: K_j at stage offset kst; HAS_PV: V_{j-1} at vst); !VCOPY:
+    // copies for tile j+2 into stage offset dst
+    auto mphase = [&](int j, int kst, int vst, int dst, auto has_qk, auto has_pv) {
+      constexpr bool QK = decltype(has_qk)::value, PV = decltype(has_pv)::value;
+      if (!VC) {
+        if (j + 2 < nkv) load_tile<C>(msrc, mdst + dst, (j + 2) * C::BC, N, lo, w);
+        if (QK) prefetch_k<C>(kpre, lo, kst);
+      }
+      tile_m<C, QK, PV>(kst, vst, lo, qr, s, p, acc, kpre);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) pin(acc[db]);
 #pragma unroll
       for (int sb = 0; sb < C::SB; ++sb) pin(s[sb]);
-      // the copies of tile j+1 (issued one step earlier) have landed; those
-      // of tile j+2 (issued in this phase) may still be in flight
-      if (j + 2 < nkv) wait_copies<C::NCOPY>();
-      else wait_copies<0>();
-      barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+      if (!VC) {
+        if (j + 2 < nkv) wait_copies<C::NI>();
+        else wait_copies<0>();
+      }
     };
-    auto softmax = [&](int j, auto mask_tag) {
+    // V(j): softmax of tile j; VCOPY: copies for tile j+3 into stage offset
+    // dst, then read ahead K of tile j+1 at stage offset kst1
+    auto vphase = [&](int j, int dst, int kst1, auto mask_tag, auto first_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
-      jumped |= tile_softmax<C, CAUSAL, MASK, EXACT>(s, p, acc, m, lsum, j * C::BC, qw0, N, c, lane);
+      constexpr bool FIRST = decltype(first_tag)::value;
+      jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST>(s, p, acc, m, lsum, j * C::BC, qw0, N, c, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (VC) {
+        if (j + 3 < nkv) {
+          load_tile<C>(msrc, mdst + dst, (j + 3) * C::BC, N, lo, w);
+          wait_copies<C::NI>();
+        } else {
+          wait_copies<0>();
+        }
+        if (j + 1 < nkv) prefetch_k<C>(kpre, lo, kst1);
+      }
       barrier();
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
     };
-    // one step with the stages of tiles j, j-1, j+2 given (compile-time
-    // constants in the unrolled loop, run-time values otherwise)
-    auto step = [&](int j, int kst, int vst, int dst, auto mask_tag) {
-      if (j + 2 < nkv) load_kv_tile<C>(dst, kh, vh, (j + 2) * C::BC, N, lo, w);
-      tile_m<C, true, true>(kst, vst, lo, qr, s, p, acc);
-      end_m(j);
-      softmax(j, mask_tag);
+    // one step; stages of tiles j, j-1, j+AHEAD, j+1 (compile-time constants
+    // in the unrolled loop, run-time values otherwise)
+    auto step = [&](int j, int kst, int vst, int dst, int kst1, auto mask_tag) {
+      mphase(j, kst, vst, dst, std::true_type{}, std::true_type{});
+      barrier();
+      vphase(j, dst, kst1, mask_tag, std::false_type{});
     };
+    constexpr int KT = C::KT;
+    auto stg = [](int t) { return (t & 3) * KT; };
 
-    load_kv_tile<C>(0, kh, vh, 0, N, lo, w);
-    if (1 < nkv) load_kv_tile<C>(C::KT, kh, vh, C::BC, N, lo, w);
+    for (int t = 0; t < AHEAD; ++t)
+      if (t < nkv) load_tile<C>(msrc, mdst + stg(t), t * C::BC, N, lo, w);
     wait_copies<0>();
     barrier();
     if (lag) barrier();
+    __builtin_amdgcn_s_setprio(1);
     // M(0), V(0)
-    if (2 < nkv) load_kv_tile<C>(2 * C::KT, kh, vh, 2 * C::BC, N, lo, w);
-    tile_m<C, true, false>(0, 0, lo, qr, s, p, acc);
-    end_m(0);
-    if (nfull > 0) softmax(0, std::false_type{});
-    else softmax(0, std::true_type{});
+    if (VC) prefetch_k<C>(kpre, lo, 0);
+    mphase(0, 0, 0, stg(AHEAD), std::true_type{}, std::false_type{});
+    barrier();
+    if (nfull > 0) vphase(0, stg(AHEAD), stg(1), std::false_type{}, std::true_type{});
+    else vphase(0, stg(AHEAD), stg(1), std::true_type{}, std::true_type{});
     // unmasked steps 1 .. j1-1, unrolled by the ring size so that every
     // stage offset is a compile-time constant (step j uses stage j % 4)
     const int j1 = max(1, min(nfull, nkv));
     int j = 1;
-    constexpr int KT = C::KT;
     for (; j + 3 < j1; j += 4) {
-      step(j + 0, 1 * KT, 0 * KT, 3 * KT, std::false_type{});
-      step(j + 1, 2 * KT, 1 * KT, 0 * KT, std::false_type{});
-      step(j + 2, 3 * KT, 2 * KT, 1 * KT, std::false_type{});
-      step(j + 3, 0 * KT, 3 * KT, 2 * KT, std::false_type{});
+      step(j + 0, stg(1), stg(0), stg(1 + AHEAD), stg(2), std::false_type{});
+      step(j + 1, stg(2), stg(1), stg(2 + AHEAD), stg(3), std::false_type{});
+      step(j + 2, stg(3), stg(2), stg(3 + AHEAD), stg(4), std::false_type{});
+      step(j + 3, stg(4), stg(3), stg(4 + AHEAD), stg(5), std::false_type{});
     }
-    if (j < j1) { step(j, 1 * KT, 0 * KT, 3 * KT, std::false_type{}); ++j; }
-    if (j < j1) { step(j, 2 * KT, 1 * KT, 0 * KT, std::false_type{}); ++j; }
-    if (j < j1) { step(j, 3 * KT, 2 * KT, 1 * KT, std::false_type{}); ++j; }
+    if (j < j1) { step(j, stg(1), stg(0), stg(1 + AHEAD), stg(2), std::false_type{}); ++j; }
+    if (j < j1) { step(j, stg(2), stg(1), stg(2 + AHEAD), stg(3), std::false_type{}); ++j; }
+    if (j < j1) { step(j, stg(3), stg(2), stg(3 + AHEAD), stg(4), std::false_type{}); ++j; }
     // remaining (masked) steps, stages at run time
-    for (; j < nkv; ++j)
-      step(j, (j & 3) * KT, ((j - 1) & 3) * KT, ((j + 2) & 3) * KT, std::true_type{});
+    for (; j < nkv; ++j) step(j, stg(j), stg(j - 1), stg(j + AHEAD), stg(j + 1), std::true_type{});
     // M(nkv): the last P V
-    tile_m<C, false, true>(0, ((nkv - 1) & 3) * KT, lo, qr, s, p, acc);
+    mphase(nkv, 0, stg(nkv - 1), 0, std::false_type{}, std::true_type{});
     if (!lag) barrier();
     barrier();  // every wave is done with the LDS ring before it is refilled
 
     // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
     const float lt = half_sum(lsum);
+    // a row is marked when either half of its keys flagged a jump
+    jumped = half_max(jumped ? 1.f : 0.f) != 0.f;
     const float inv = 1.f / lt;
     const int query = qw0 + l32;
     if (query < N && (!EXACT || mine)) {  // the recompute kernel stores only marked rows
