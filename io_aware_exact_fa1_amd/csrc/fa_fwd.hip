@@ -620,37 +620,150 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     constexpr int KT = C::KT;
     auto stg = [](int t) { return (t & 3) * KT; };
 
-    for (int t = 0; t < AHEAD; ++t)
-      if (t < nkv) load_tile<C>(msrc, mdst + stg(t), t * C::BC, N, lo, w);
-    wait_copies<0>();
-    barrier();
-    if (lag) barrier();
-    __builtin_amdgcn_s_setprio(1);
-    // M(0), V(0)
-    if (VC) prefetch_k<C>(kpre, lo, 0);
-    mphase(0, 0, 0, stg(AHEAD), std::true_type{}, std::false_type{});
-    barrier();
-    if (nfull > 0) vphase(0, stg(AHEAD), stg(1), std::false_type{}, std::true_type{});
-    else vphase(0, stg(AHEAD), stg(1), std::true_type{}, std::true_type{});
-    // unmasked steps 1 .. j1-1, unrolled by the ring size so that every
-    // stage offset is a compile-time constant (step j uses stage j % 4)
-    const int j1 = max(1, min(nfull, nkv));
-    int j = 1;
-    for (; j + 3 < j1; j += 4) {
-      step(j + 0, stg(1), stg(0), stg(1 + AHEAD), stg(2), std::false_type{});
-      step(j + 1, stg(2), stg(1), stg(2 + AHEAD), stg(3), std::false_type{});
-      step(j + 2, stg(3), stg(2), stg(3 + AHEAD), stg(4), std::false_type{});
-      step(j + 3, stg(4), stg(3), stg(4 + AHEAD), stg(5), std::false_type{});
+    if constexpr (VC) {
+      // One barrier per step.  Between barriers j and j+1 (window j) the
+      // leading half runs V(j) then M(j+1), the lagging half M(j) then V(j):
+      // each SIMD still alternates a matrix phase of one wave with the
+      // vector phase of the other, with half the synchronisation.  In window
+      // j the leading half copies K_{j+3} (into the stage of K_{j-1}, whose
+      // last reads were in window j-1) and waits for K_{j+2}; the lagging
+      // half copies V_{j+2} (stage of V_{j-2}, last read in window j-1) and
+      // waits for V_{j+1}.  So K_t and V_t are complete by barrier t-1, and
+      // the first reads of tile t -- the read-ahead of K_t in window t-1 and
+      // the leading P V of tile t in window t+1 -- come after it.
+      auto m1 = [&](int kst, int vst, auto has_qk, auto has_pv) {
+        constexpr bool QK = decltype(has_qk)::value, PV = decltype(has_pv)::value;
+        tile_m<C, QK, PV>(kst, vst, lo, qr, s, p, acc, kpre);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) pin(acc[db]);
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb) pin(s[sb]);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // V(j) with the stages of tiles j+1, j+2, j+3 (LAG: this wave is in the
+      // lagging half, which copies V; the leading half copies K)
+      auto v1 = [&](int j, int s1, int s2, int s3, auto lag_tag, auto mask_tag, auto first_tag) {
+        constexpr bool LAG = decltype(lag_tag)::value;
+        constexpr bool MASK = decltype(mask_tag)::value;
+        constexpr bool FIRST = decltype(first_tag)::value;
+        jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST>(s, p, acc, m, lsum, j * C::BC, qw0, N, c, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        const int ct = LAG ? j + 2 : j + 3;  // the tile this wave copies now
+        if (ct < nkv) {
+          load_tile<C>(LAG ? vh : kh, lo.base + (LAG ? C::VBASE + s2 : s3), ct * C::BC, N, lo, w);
+          wait_copies<C::NI>();
+        } else {
+          wait_copies<0>();
+        }
+        if (j + 1 < nkv) prefetch_k<C>(kpre, lo, s1);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // the whole key loop of one half (each half gets its own copy of the
+      // code, so that the register allocation follows its own phase order)
+      auto run = [&](auto lag_tag) {
+        constexpr bool LAG = decltype(lag_tag)::value;
+        const std::true_type T{};
+        const std::false_type F{};
+        // window j for 1 <= j < nkv - 1, stages of tiles j-1 .. j+3
+        auto window = [&](int j, int sm1, int s0, int s1, int s2, int s3, auto mask_tag) {
+          if (!LAG) {
+            v1(j, s1, s2, s3, lag_tag, mask_tag, F);
+            m1(s1, s0, T, T);
+          } else {
+            m1(s0, sm1, T, T);
+            v1(j, s1, s2, s3, lag_tag, mask_tag, F);
+          }
+          barrier();
+        };
+        for (int t = 0; t < (LAG ? 2 : 3); ++t)
+          if (t < nkv) load_tile<C>(LAG ? vh : kh, lo.base + (LAG ? C::VBASE : 0) + stg(t), t * C::BC, N, lo, w);
+        wait_copies<0>();
+        barrier();
+        prefetch_k<C>(kpre, lo, 0);
+        __builtin_amdgcn_s_setprio(1);
+        if (!LAG) m1(0, 0, T, F);  // leading M(0)
+        barrier();
+        // window 0 (its tile may need the mask: the mask is exact on any tile)
+        if (!LAG) {
+          v1(0, stg(1), stg(2), stg(3), lag_tag, T, T);
+          if (1 < nkv) m1(stg(1), stg(0), T, T);
+          else m1(0, stg(0), F, T);
+        } else {
+          m1(0, 0, T, F);
+          v1(0, stg(1), stg(2), stg(3), lag_tag, T, T);
+        }
+        barrier();
+        // unmasked windows 1 .. j1-1, unrolled by the ring size so that
+        // every stage offset is a compile-time constant
+        const int j1 = max(1, min(nfull, nkv - 1));
+        int j = 1;
+        for (; j + 3 < j1; j += 4) {
+          window(j + 0, stg(0), stg(1), stg(2), stg(3), stg(4), F);
+          window(j + 1, stg(1), stg(2), stg(3), stg(4), stg(5), F);
+          window(j + 2, stg(2), stg(3), stg(4), stg(5), stg(6), F);
+          window(j + 3, stg(3), stg(4), stg(5), stg(6), stg(7), F);
+        }
+        if (j < j1) { window(j, stg(0), stg(1), stg(2), stg(3), stg(4), F); ++j; }
+        if (j < j1) { window(j, stg(1), stg(2), stg(3), stg(4), stg(5), F); ++j; }
+        if (j < j1) { window(j, stg(2), stg(3), stg(4), stg(5), stg(6), F); ++j; }
+        // masked windows up to nkv - 2, stages at run time
+        for (; j < nkv - 1; ++j) window(j, stg(j - 1), stg(j), stg(j + 1), stg(j + 2), stg(j + 3), T);
+        // the last window (nkv >= 2): the leading half's M(nkv) is P V only
+        if (nkv >= 2) {
+          const int jl = nkv - 1;
+          if (!LAG) {
+            v1(jl, stg(jl + 1), stg(jl + 2), stg(jl + 3), lag_tag, T, F);
+            m1(0, stg(jl), F, T);
+          } else {
+            m1(stg(jl), stg(jl - 1), T, T);
+            v1(jl, stg(jl + 1), stg(jl + 2), stg(jl + 3), lag_tag, T, F);
+          }
+          barrier();
+        }
+        // the lagging half's M(nkv): the last P V
+        if (LAG) m1(0, stg(nkv - 1), F, T);
+      };
+      if (lag) run(std::true_type{});
+      else run(std::false_type{});
+      barrier();  // every wave is done with the LDS ring before it is refilled
+    } else {
+
+      for (int t = 0; t < AHEAD; ++t)
+        if (t < nkv) load_tile<C>(msrc, mdst + stg(t), t * C::BC, N, lo, w);
+      wait_copies<0>();
+      barrier();
+      if (lag) barrier();
+      __builtin_amdgcn_s_setprio(1);
+      // M(0), V(0)
+      if (VC) prefetch_k<C>(kpre, lo, 0);
+      mphase(0, 0, 0, stg(AHEAD), std::true_type{}, std::false_type{});
+      barrier();
+      if (nfull > 0) vphase(0, stg(AHEAD), stg(1), std::false_type{}, std::true_type{});
+      else vphase(0, stg(AHEAD), stg(1), std::true_type{}, std::true_type{});
+      // unmasked steps 1 .. j1-1, unrolled by the ring size so that every
+      // stage offset is a compile-time constant (step j uses stage j % 4)
+      const int j1 = max(1, min(nfull, nkv));
+      int j = 1;
+      for (; j + 3 < j1; j += 4) {
+        step(j + 0, stg(1), stg(0), stg(1 + AHEAD), stg(2), std::false_type{});
+        step(j + 1, stg(2), stg(1), stg(2 + AHEAD), stg(3), std::false_type{});
+        step(j + 2, stg(3), stg(2), stg(3 + AHEAD), stg(4), std::false_type{});
+        step(j + 3, stg(4), stg(3), stg(4 + AHEAD), stg(5), std::false_type{});
+      }
+      if (j < j1) { step(j, stg(1), stg(0), stg(1 + AHEAD), stg(2), std::false_type{}); ++j; }
+      if (j < j1) { step(j, stg(2), stg(1), stg(2 + AHEAD), stg(3), std::false_type{}); ++j; }
+      if (j < j1) { step(j, stg(3), stg(2), stg(3 + AHEAD), stg(4), std::false_type{}); ++j; }
+      // remaining (masked) steps, stages at run time
+      for (; j < nkv; ++j) step(j, stg(j), stg(j - 1), stg(j + AHEAD), stg(j + 1), std::true_type{});
+      // M(nkv): the last P V
+      mphase(nkv, 0, stg(nkv - 1), 0, std::false_type{}, std::true_type{});
+      if (!lag) barrier();
+      barrier();  // every wave is done with the LDS ring before it is refilled
     }
-    if (j < j1) { step(j, stg(1), stg(0), stg(1 + AHEAD), stg(2), std::false_type{}); ++j; }
-    if (j < j1) { step(j, stg(2), stg(1), stg(2 + AHEAD), stg(3), std::false_type{}); ++j; }
-    if (j < j1) { step(j, stg(3), stg(2), stg(3 + AHEAD), stg(4), std::false_type{}); ++j; }
-    // remaining (masked) steps, stages at run time
-    for (; j < nkv; ++j) step(j, stg(j), stg(j - 1), stg(j + AHEAD), stg(j + 1), std::true_type{});
-    // M(nkv): the last P V
-    mphase(nkv, 0, stg(nkv - 1), 0, std::false_type{}, std::true_type{});
-    if (!lag) barrier();
-    barrier();  // every wave is done with the LDS ring before it is refilled
 
     // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
     const float lt = half_sum(lsum);
