@@ -7,12 +7,18 @@ its Python binding never do, and the oracle never imports them.
   * ``ref``   - the plain definition, score matrix materialised.
   * ``tiled`` - the Q-outer online-softmax recurrence with tile sizes as
                 arguments, used to pin the recurrence to the definition.
+  * ``backward`` - the gradients dQ, dK, dV of the forward, from the plain
+                definition and in the recomputation form (P from the saved
+                LSE, D = O . dO).
 """
 
 from .ref import as_f64, scores_ref, probabilities_ref, attention_ref, attention_rows_ref
 from .tiled import tiled_ref
+from .backward import (attention_bwd_ref, attention_bwd_from_lse_ref, attention_bwd_rows_ref,
+                       attention_bwd_cols_ref)
 
 __all__ = [
     "as_f64", "scores_ref", "probabilities_ref", "attention_ref",
-    "attention_rows_ref", "tiled_ref",
+    "attention_rows_ref", "tiled_ref", "attention_bwd_ref", "attention_bwd_from_lse_ref",
+    "attention_bwd_rows_ref", "attention_bwd_cols_ref",
 ]
