@@ -113,6 +113,49 @@ const char* fa_strerror(int status);
 int fa_check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   int B, int H, int N, int d, float scale, int causal, int elem_bytes);
 
+/*
+ * Backward pass of fa_fwd (bf16): the gradients dQ, dK, dV of sum(O * dO)
+ * with respect to Q, K, V, recomputed from Q, K, V and the forward's LSE
+ * instead of a stored probability matrix.
+ *
+ * What is computed, per (b, h), following "FlashAttention：从 IO-Aware
+ * Attention 到 GPU Work Partitioning" (blog.euler0525.cn), sections
+ * "Tiling、Fusion 与 Backward Recomputation" and "减少 Non-Matmul FLOPs", and
+ * "FlashAttention V1" (infra.bea.ai), section "5. The Backward Pass":
+ *   P  = exp(scale * Q K^T - LSE)   (causal: 0 where key > query)
+ *   D_i = O_i . dO_i
+ *   dS = P * (dO V^T - D)
+ *   dV = P^T dO,  dQ = scale * dS K,  dK = scale * dS^T Q
+ * (the pages write the gradients for unscaled scores; the scale of the
+ * forward enters dQ and dK once by the chain rule).
+ *
+ * Arguments:
+ *   q, k, v, o, dout  bf16 [B, H, N, d] contiguous, device memory, read only:
+ *                     the forward's inputs and output (O as fa_fwd wrote
+ *                     it) and the upstream gradient dO.
+ *   lse               fp32 [B, H, N], the natural-log LSE fa_fwd wrote.
+ *   dq, dk, dv        bf16 [B, H, N, d], written entirely (outputs).
+ *   delta             fp32 [B, H, N] workspace owned by the caller; on
+ *                     return it holds D_i = O_i . dO_i.
+ *   B, H, N, d, scale, causal, stream: as for fa_fwd (scale and causal must
+ *                     be those of the forward call).
+ * Layout, ownership, stream semantics and error codes as for fa_fwd; in
+ * addition dq, dk, dv and delta must not overlap each other or any input
+ * (FA_ERR_ALIAS).  The two kernels run in order on `stream`; nothing is
+ * allocated and no atomics are used, so results are deterministic.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, float* delta, int B, int H, int N, int d, float scale, int causal,
+           hipStream_t stream);
+
+/*
+ * Host-side argument check of fa_bwd without any HIP call: returns the
+ * status fa_bwd would return before launching.
+ */
+int fa_bwd_check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, const void* dq, const void* dk, const void* dv, const float* delta,
+                      int B, int H, int N, int d, float scale, int causal);
+
 #ifdef __cplusplus
 }
 #endif

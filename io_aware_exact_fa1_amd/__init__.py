@@ -1,4 +1,4 @@
-"""MI355X-native exact attention forward (FlashAttention forward pass).
+"""MI355X-native exact attention (FlashAttention forward pass and its backward).
 
 The computation lives in the HIP library ``libfa_mi355x.so`` (sources in
 ``csrc/``, C ABI in ``include/fa.h``); this package is its thin ctypes
@@ -7,6 +7,6 @@ binding.  PyTorch is used only for device buffers and streams.
 
 from ._binding import (  # noqa: F401
     EXPORTED, FA_ERR_ALIAS, FA_ERR_ALIGN, FA_ERR_HEAD_DIM, FA_ERR_LAUNCH, FA_ERR_NULL, FA_ERR_SCALE,
-    FA_ERR_SHAPE, FA_OK, LIB_PATH, FaError, fa_check_args, fa_fwd, fa_fwd_f32, fa_strerror, forward,
-    load_library,
+    FA_ERR_SHAPE, FA_OK, LIB_PATH, FaError, backward, fa_bwd, fa_bwd_check_args, fa_check_args, fa_fwd,
+    fa_fwd_f32, fa_strerror, forward, load_library,
 )

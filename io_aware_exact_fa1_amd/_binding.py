@@ -1,7 +1,8 @@
 """ctypes binding of the C ABI in ``include/fa.h`` (argument marshalling only).
 
-The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_strerror`` and ``fa_check_args``
-have the names and argument order of the C entry points; tensors are passed
+The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_bwd``, ``fa_strerror``,
+``fa_check_args`` and ``fa_bwd_check_args`` have the names and argument
+order of the C entry points; tensors are passed
 as their device pointers and streams as HIP stream handles.  Every step of
 the computation runs in the HIP library: there is no fallback path, and a
 missing or unloadable library raises.
@@ -23,7 +24,7 @@ FA_ERR_ALIAS = 5
 FA_ERR_LAUNCH = 6
 FA_ERR_ALIGN = 7
 
-EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_check_args")
+EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_strerror", "fa_check_args", "fa_bwd_check_args")
 
 _lib = None
 
@@ -59,6 +60,10 @@ def load_library(path=None):
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i]
     lib.fa_check_args.restype = i
+    lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_check_args.argtypes = [vp] * 10 + [i, i, i, i, f, i]
+    lib.fa_bwd_check_args.restype = i
     if path is None:
         _lib = lib
     return lib
@@ -91,6 +96,19 @@ def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
     """C ``fa_fwd_f32``: fp32 q, k, v, o and lse; returns the status code."""
     return load_library().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                                      int(N), int(d), float(scale), int(causal), _stream(stream))
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream=None):
+    """C ``fa_bwd``: bf16 q, k, v, o, dout, dq, dk, dv; fp32 lse and delta."""
+    return load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), _ptr(delta), int(B), int(H), int(N), int(d),
+                                 float(scale), int(causal), _stream(stream))
+
+
+def fa_bwd_check_args(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal):
+    return load_library().fa_bwd_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), int(B), int(H),
+                                            int(N), int(d), float(scale), int(causal))
 
 
 def fa_strerror(status):
@@ -136,3 +154,34 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
     if st != FA_OK:
         raise FaError(st, where)
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
+    """Allocate dQ, dK, dV and the D workspace with torch, call ``fa_bwd``,
+    raise FaError on a nonzero status; returns (dQ, dK, dV, D).
+
+    q, k, v, o, dout: bfloat16 CUDA tensors [B, H, N, d]; lse: float32
+    [B, H, N] from the forward with the same causal and scale.
+    """
+    import math
+    import torch
+    ts = (q, k, v, o, dout)
+    if not all(x.is_cuda for x in ts + (lse,)):
+        raise ValueError("all tensors must be GPU tensors")
+    if any(x.shape != q.shape for x in ts) or q.dim() != 4:
+        raise ValueError("q, k, v, o and dout must share one [B, H, N, d] shape")
+    if any(x.dtype != torch.bfloat16 for x in ts) or lse.dtype != torch.float32:
+        raise ValueError("q, k, v, o, dout must be bfloat16 and lse float32")
+    B, H, N, d = q.shape
+    if tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be [B, H, N]")
+    q, k, v, o, dout, lse = (x.contiguous() for x in (q, k, v, o, dout, lse))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv, delta

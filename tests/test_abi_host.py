@@ -24,7 +24,8 @@ def declared_functions():
 
 
 def test_header_declares_the_abi():
-    assert declared_functions() == sorted(["fa_check_args", "fa_fwd", "fa_fwd_f32", "fa_strerror"])
+    assert declared_functions() == sorted(["fa_bwd", "fa_bwd_check_args", "fa_check_args", "fa_fwd",
+                                           "fa_fwd_f32", "fa_strerror"])
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -92,3 +93,51 @@ def test_forward_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(x, x, x)
+
+
+# backward: fake addresses of o, dout, dq, dk, dv, delta
+DO, DQ, DK, DV, DL = (0x10000000 * (i + 6) for i in range(5))
+
+
+def _bwd(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, dout=DO, dq=DQ, dk=DK, dv=DV, delta=DL, B=1, H=2, N=40, d=64,
+             scale=0.125, causal=1)
+    a.update(kw)
+    return fa.fa_bwd_check_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                                a["delta"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["causal"])
+
+
+def test_bwd_check_args_ok():
+    assert _bwd() == fa.FA_OK
+    assert _bwd(d=128, causal=0, scale=-1.0) == fa.FA_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), fa.FA_ERR_SHAPE),
+    (dict(d=80), fa.FA_ERR_HEAD_DIM),
+    (dict(scale=math.inf), fa.FA_ERR_SCALE),
+    (dict(dout=None), fa.FA_ERR_NULL),
+    (dict(delta=None), fa.FA_ERR_NULL),
+    (dict(dq=DQ + 8), fa.FA_ERR_ALIGN),
+    (dict(delta=DL + 2), fa.FA_ERR_ALIGN),
+    (dict(dq=Q), fa.FA_ERR_ALIAS),          # output over an input
+    (dict(dv=DK), fa.FA_ERR_ALIAS),         # two outputs overlap
+    (dict(delta=L), fa.FA_ERR_ALIAS),       # workspace over the forward's LSE
+    (dict(delta=DQ + 64), fa.FA_ERR_ALIAS),
+])
+def test_bwd_check_args_errors(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_bwd_rejects_and_noops_on_the_host():
+    assert fa.fa_bwd(Q, K, V, O, L, DO, DQ, DK, DV, DL, 1, 1, 8, 96, 1.0, 0, 0) == fa.FA_ERR_HEAD_DIM
+    assert fa.fa_bwd(*([None] * 10), 0, 3, 16, 64, 1.0, 1, 0) == fa.FA_OK
+
+
+def test_backward_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError):
+        fa.backward(x, x, x, x, lse, x)
+
