@@ -15,7 +15,12 @@ causal, with Q/K/V already resident in HBM.  Prints ONE JSON line:
   cpu_baseline            the fp64 CPU oracle timed on a bounded sample of
                           the same workload on this host's cores
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+With --backward, a step is one ``fa_bwd`` call (dQ, dK, dV recomputed from
+the forward's O and LSE) on the same workload instead; FLOPs are counted as
+2.5 times the forward's (the five N x N x d products of the backward, the
+recomputation of S included).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--backward]
 """
 
 import argparse
@@ -48,6 +53,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--backward", action="store_true",
+                   help="time the backward pass (fa_bwd) instead of the forward")
     p.add_argument("--copy-cal", action="store_true",
                    help="run only a plain device copy of 1 GiB (5 times), to calibrate the HBM "
                         "byte counters (FETCH_SIZE / WRITE_SIZE) of a profiler run")
@@ -135,6 +142,47 @@ def cpu_baseline(w, q, k, v, target_s):
     }
 
 
+def cpu_baseline_bwd(w, q, k, v, do, target_s):
+    """Time the fp64 backward oracle (as it stands) on a bounded sample of the
+    same workload: whole heads, dQ of every query row computed on its own
+    (S, dP and dQ of the row: 6 * keys * d FLOPs), until about ``target_s``
+    seconds of CPU work have been done."""
+    import numpy as np
+    import torch
+    from oracle import attention_bwd_rows_ref  # CPU baseline leg only
+
+    rows = np.arange(w.N)
+    flops, heads, nrows, el = 0.0, 0, 0, 0.0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            qh, kh, vh, dh = (x[b, h].to(torch.float64).numpy() for x in (q, k, v, do))
+            for i in range(0, w.N, 256):
+                sel = rows[i:i + 256]
+                attention_bwd_rows_ref(qh, kh, vh, dh, w.scale, w.causal, sel)
+                keys = (sel + 1) if w.causal else np.full(sel.size, w.N)
+                flops += 6.0 * float(keys.sum()) * w.d
+                nrows += sel.size
+                el = time.perf_counter() - t0
+                if el >= target_s:
+                    break
+            heads += 1
+            if el >= target_s:
+                break
+        if el >= target_s:
+            break
+    cores = len(os.sched_getaffinity(0))
+    return {
+        "value": flops / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"{nrows} query rows of {heads} head(s) of {w.name}: dQ of each row computed on its own by "
+                   f"the fp64 numpy backward oracle (attention_bwd_rows_ref), {el:.1f} s wall; "
+                   f"{cores} host cores visible"),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -173,6 +221,27 @@ def main():
         if st != fa.FA_OK:
             raise fa.FaError(st, "fa_fwd")
 
+    flops = w.flops
+    do = None
+    if args.backward:
+        if w.dtype != "bf16":
+            log("--backward needs a bf16 workload")
+            sys.exit(2)
+        g = torch.Generator(device="cpu")
+        g.manual_seed(w.seed + 7919)
+        do = torch.randn(q.shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+        dod = do.to(dev)
+        dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+        delta = torch.empty_like(lse)
+        step()  # O and LSE of the forward
+        flops = 2.5 * w.flops
+
+        def step():
+            st = fa.fa_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, delta, w.B, w.H, w.N, w.d, w.scale,
+                           int(w.causal), sh)
+            if st != fa.FA_OK:
+                raise fa.FaError(st, "fa_bwd")
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -194,23 +263,29 @@ def main():
     avg_ms = sum(launch_ms) / len(launch_ms)
     med_ms = launch_ms[len(launch_ms) // 2]
     ms_per_step = wall * 1e3 / args.steps
-    tflop = w.flops / 1e12
+    tflop = flops / 1e12
     value = tflop / (ms_per_step / 1e3)
     achieved = tflop / (avg_ms / 1e3)
     log(f"[bench] {w.name}: wall {ms_per_step:.3f} ms/step, kernel avg {avg_ms:.3f} ms "
         f"(median {med_ms:.3f}, min {launch_ms[0]:.3f}) -> {achieved:.1f} TFLOP/s "
         f"= {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 dense peak")
 
-    traffic = measured_traffic(w.name)
+    traffic = None if args.backward else measured_traffic(w.name)
 
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on a sample (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        if args.backward:
+            cpu = cpu_baseline_bwd(w, q, k, v, do, args.cpu_seconds)
+        else:
+            cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
         log(f"[bench] cpu baseline {cpu['value'] * 1e3:.3f} GFLOP/s ({cpu['sample']})")
 
+    metric = "attn fwd TFLOP/s + % bf16 MFMA peak, N=16K d=128 causal (1 MI355X)"
+    if args.backward:
+        metric = "attn bwd TFLOP/s (2.5x fwd FLOPs) + % bf16 MFMA peak (1 MI355X)"
     out = {
-        "metric": "attn fwd TFLOP/s + % bf16 MFMA peak, N=16K d=128 causal (1 MI355X)",
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -223,7 +298,8 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "scale": w.scale, "flops_per_step": w.flops, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+                   "scale": w.scale, "pass": "backward" if args.backward else "forward",
+                   "flops_per_step": flops, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,

@@ -25,9 +25,10 @@
 //    dQ^T += K^T dS^T with K^T read from the LDS tile by transpose reads and
 //    dS^T (bf16) as the register operand.  It also forms D_i = O_i . dO_i
 //    for its rows and writes D to the caller's workspace.
-//  * dK/dV kernel (key-tiled): a workgroup owns 128 keys (4 waves x 32, K
-//    and V rows in registers) and streams 32-query tiles of Q, dO and their
-//    L and D through LDS.  Per tile: S = Q K^T and dP = dO V^T with one key
+//  * dK/dV kernel (key-tiled): a workgroup owns 128 keys (4 waves x 32; K
+//    rows in registers, V rows resident in LDS, so that two workgroups fit
+//    on a CU) and streams 32-query tiles of Q, dO and their L and D through
+//    LDS.  Per tile: S = Q K^T and dP = dO V^T with one key
 //    per lane, P and dS in registers, then dV^T += dO^T P and
 //    dK^T += Q^T dS with dO^T and Q^T read by transpose reads.
 //  Both use the LDS swizzle and the operand layouts of the forward kernel,
@@ -297,13 +298,14 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 // ---------------------------------------------------------------------------
 // dK/dV kernel: key-tiled.
 template <class C, bool CAUSAL>
-__global__ void __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const float* __restrict__ lse,
                    const uint16_t* __restrict__ dout, const float* __restrict__ delta, uint16_t* __restrict__ dk,
                    uint16_t* __restrict__ dv, int N, int T_r, int units_per_head, int num_units, int per_xcd,
                    float c, float scale) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
+  // two stages of (Q, dO, L, D) tiles, then the V rows of the workgroup's keys
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE + C::ROWS * C::ROWB];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
@@ -329,16 +331,18 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int key = k0 + w * 32 + l32;
     const int krow = min(key, N - 1);
 
-    // K and V rows as register operands (lane: key l%32, dims 16 kb + 8h ..)
-    bf16x8 kr[C::KB], vr[C::KB];
+    // K rows as register operands (lane: key l%32, dims 16 kb + 8h ..); the
+    // V rows of the workgroup's keys go to LDS (32-row tile w holds wave w's)
+    bf16x8 kr[C::KB];
     {
       const size_t ro = hoff + (size_t)krow * C::D + 8 * h;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        kr[kb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(k + ro + 16 * kb));
-        vr[kb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(v + ro + 16 * kb));
-      }
+      for (int kb = 0; kb < C::KB; ++kb) kr[kb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(k + ro + 16 * kb));
     }
+    const unsigned vres = lbase + 2 * C::STAGE;
+#pragma unroll
+    for (int t = 0; t < C::NW; ++t) copy_tile<C>(v + hoff, vres + t * C::TB, k0 + t * C::T, N, bl, w);
+    const unsigned vmine = vres + w * C::TB;
     f32x16 dka[C::DB], dva[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -379,7 +383,7 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         s = mfma(lds_row(qt + bl.row[kb]), kr[kb], s);
-        dp = mfma(lds_row(ot + bl.row[kb]), vr[kb], dp);
+        dp = mfma(lds_row(ot + bl.row[kb]), lds_row(vmine + bl.row[kb]), dp);
       }
       // L (as log2) and D of this lane's 16 queries
       float lq[16], dq16[16];
