@@ -20,7 +20,14 @@ the forward's O and LSE) on the same workload instead; FLOPs are counted as
 2.5 times the forward's (the five N x N x d products of the backward, the
 recomputation of S included).
 
+With --shapes "B,H,N,d,causal;...", each listed shape (bf16, seeded N(0,1)
+inputs) is run in turn and one JSON line per shape is printed with its time
+and the two byte models of the pages (read-once bytes and tile-stream
+bytes); run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE this gives the
+measured HBM bytes of each shape (one dispatch of the main kernel per step).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--backward]
+       python bench.py --shapes "1,64,4096,128,1;1,64,8192,64,0" [--steps K] [--warmup W]
 """
 
 import argparse
@@ -55,6 +62,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--backward", action="store_true",
                    help="time the backward pass (fa_bwd) instead of the forward")
+    p.add_argument("--shapes", default=None,
+                   help="semicolon-separated B,H,N,d,causal shapes to run one after the other (forward, bf16)")
     p.add_argument("--copy-cal", action="store_true",
                    help="run only a plain device copy of 1 GiB (5 times), to calibrate the HBM "
                         "byte counters (FETCH_SIZE / WRITE_SIZE) of a profiler run")
@@ -183,6 +192,48 @@ def cpu_baseline_bwd(w, q, k, v, do, target_s):
     }
 
 
+def shape_sweep(args):
+    """One JSON line per shape: forward time and the byte models."""
+    import torch
+    import io_aware_exact_fa1_amd as fa
+    import workloads
+
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    for spec in args.shapes.split(";"):
+        B, H, N, d, causal = (int(x) for x in spec.split(","))
+        q, k, v = workloads.make_qkv(B, H, N, d, torch.bfloat16, 1000 + N + d)
+        qd, kd, vd = (x.to(dev) for x in (q, k, v))
+        o = torch.empty_like(qd)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        scale = 1.0 / math.sqrt(d)
+
+        def step():
+            st = fa.fa_fwd(qd, kd, vd, o, lse, B, H, N, d, scale, causal, stream.cuda_stream)
+            if st != fa.FA_OK:
+                raise fa.FaError(st, "fa_fwd")
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        flops = 4.0 * B * H * N * N * d / (2 if causal else 1)
+        br, bc = 256, (64 if d == 128 else 128)
+        print(json.dumps({"shape": {"B": B, "H": H, "N": N, "d": d, "causal": bool(causal)},
+                          "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                          "once_bytes": workloads.hbm_once_bytes(B, H, N, d),
+                          "stream_bytes": workloads.tile_stream_bytes(B, H, N, d, br, bc, bool(causal)),
+                          "tile": {"Br": br, "Bc": bc}}), flush=True)
+        del qd, kd, vd, o, lse
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -193,6 +244,9 @@ def main():
 
     if args.copy_cal:
         copy_calibration()
+        return
+    if args.shapes:
+        shape_sweep(args)
         return
 
     import torch

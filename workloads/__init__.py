@@ -18,7 +18,7 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "get"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "get", "hbm_once_bytes", "tile_stream_bytes"]
 
 
 @dataclass(frozen=True)
@@ -114,3 +114,30 @@ def sample_heads(B, H, count, seed):
     count = min(count, B * H)
     flat = np.sort(rng.choice(B * H, size=count, replace=False))
     return [(int(f) // H, int(f) % H) for f in flat]
+
+
+# ---------------------------------------------------------------- byte models
+def hbm_once_bytes(B, H, N, d, elt=2):
+    """Bytes a forward must move between HBM and the chip when every input
+    row is read once and every output row written once: Q, K, V read, O
+    written (elt bytes per element) and the fp32 LSE written.  The model of
+    "FlashAttention V1" (infra.bea.ai), section "4. Memory Analysis", plus
+    the LSE."""
+    return 4 * B * H * N * d * elt + 4 * B * H * N
+
+
+def tile_stream_bytes(B, H, N, d, Br, Bc, causal, elt=2):
+    """Bytes the tiled forward requests from memory when nothing is reused
+    across query tiles: Q once, every visible K and V tile once per query
+    tile of Br rows, O and the fp32 LSE once.  The count of "Lecture 3 —
+    FlashAttention-1 Algorithm" (jared-hpc.com), section "Why this is
+    O(N^2 d^2 / M) bytes", with the causal loop bound (query tile i reads key
+    tiles 0 .. ceil(min(N, (i+1) Br) / Bc) - 1)."""
+    tr = -(-N // Br)
+    tc = -(-N // Bc)
+    kv_tiles = 0
+    for i in range(tr):
+        kv_tiles += -(-min(N, (i + 1) * Br) // Bc) if causal else tc
+    per_head = N * d * elt + kv_tiles * 2 * Bc * d * elt + N * d * elt + 4 * N
+    return B * H * per_head
+
