@@ -10,15 +10,19 @@ its Python binding never do, and the oracle never imports them.
   * ``backward`` - the gradients dQ, dK, dV of the forward, from the plain
                 definition and in the recomputation form (P from the saved
                 LSE, D = O . dO).
+  * ``variants`` - grouped K/V heads, queries at an offset into a longer
+                key sequence, and a sliding window.
 """
 
 from .ref import as_f64, scores_ref, probabilities_ref, attention_ref, attention_rows_ref
 from .tiled import tiled_ref
+from .variants import attention_ex_ref, attention_ex_rows_ref, visible_mask
 from .backward import (attention_bwd_ref, attention_bwd_from_lse_ref, attention_bwd_rows_ref,
                        attention_bwd_cols_ref)
 
 __all__ = [
     "as_f64", "scores_ref", "probabilities_ref", "attention_ref",
     "attention_rows_ref", "tiled_ref", "attention_bwd_ref", "attention_bwd_from_lse_ref",
-    "attention_bwd_rows_ref", "attention_bwd_cols_ref",
+    "attention_bwd_rows_ref", "attention_bwd_cols_ref", "attention_ex_ref", "attention_ex_rows_ref",
+    "visible_mask",
 ]
