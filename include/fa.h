@@ -65,7 +65,8 @@ enum fa_status {
     FA_ERR_SCALE = 4,     /* scale is NaN or infinite                       */
     FA_ERR_ALIAS = 5,     /* O or LSE overlaps Q, K, V or each other        */
     FA_ERR_LAUNCH = 6,    /* the HIP launch reported an error               */
-    FA_ERR_ALIGN = 7      /* a pointer is not aligned to 16 bytes           */
+    FA_ERR_ALIGN = 7,     /* a pointer is not aligned to 16 bytes           */
+    FA_ERR_VARIANT = 8    /* fa_fwd_ex: Hq % Hkv != 0, S == 0, bad offset or window */
 };
 
 /*
@@ -112,6 +113,40 @@ const char* fa_strerror(int status);
  */
 int fa_check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
                   int B, int H, int N, int d, float scale, int causal, int elem_bytes);
+
+/*
+ * Variants of fa_fwd (bf16): grouped K/V heads (GQA), queries at an offset
+ * into a longer key sequence (chunked prefill, decode), a sliding window.
+ *
+ * What is computed, following "15. FlashAttention"
+ * (inference.shantanugoel.com), section "The kernel": query head h of
+ * batch b reads K/V head h / (Hq / Hkv); query row i sits at absolute
+ * position offset + i; key j is visible to row i iff j < S and, when causal,
+ * j <= offset + i and, with a window W > 0, j >= offset + i - W + 1 (the
+ * window covers W keys ending at the query's own position; it requires the
+ * causal mask).  Then O = softmax(scale * q k^T over the visible keys) v and
+ * LSE = logsumexp of those scores, per row.
+ *
+ * Arguments:
+ *   q, o   bf16 [B, Hq, T, d] contiguous device memory (q read, o written).
+ *   k, v   bf16 [B, Hkv, S, d] contiguous device memory, read only.
+ *   lse    fp32 [B, Hq, T], natural log, written.
+ *   offset position of query row 0 (causal only; ignored otherwise), with
+ *          0 <= offset <= S - T so that no row is empty; S - T is the usual
+ *          choice (the queries are the newest positions).
+ *   window 0 for none, else W >= 1 (causal only).
+ *   B, d, scale, causal, stream: as for fa_fwd.
+ * Errors as for fa_fwd, plus FA_ERR_VARIANT for Hq % Hkv != 0, S == 0, an
+ * offset outside [0, S - T] or a window without the causal mask.  With
+ * Hq == Hkv, T == S, offset 0 and no window the result equals fa_fwd's
+ * (this entry point runs the same kernel with every tile masked).
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int T,
+              int S, int d, float scale, int causal, int offset, int window, hipStream_t stream);
+
+/* Host-side argument check of fa_fwd_ex without any HIP call. */
+int fa_check_args_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int Hq,
+                     int Hkv, int T, int S, int d, float scale, int causal, int offset, int window);
 
 /*
  * Backward pass of fa_fwd (bf16): the gradients dQ, dK, dV of sum(O * dO)

@@ -1,8 +1,9 @@
 """ctypes binding of the C ABI in ``include/fa.h`` (argument marshalling only).
 
-The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_bwd``, ``fa_strerror``,
-``fa_check_args`` and ``fa_bwd_check_args`` have the names and argument
-order of the C entry points; tensors are passed
+The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_fwd_ex``, ``fa_bwd``,
+``fa_strerror``, ``fa_check_args``, ``fa_check_args_ex`` and
+``fa_bwd_check_args`` have the names and argument order of the C entry
+points; tensors are passed
 as their device pointers and streams as HIP stream handles.  Every step of
 the computation runs in the HIP library: there is no fallback path, and a
 missing or unloadable library raises.
@@ -23,8 +24,10 @@ FA_ERR_SCALE = 4
 FA_ERR_ALIAS = 5
 FA_ERR_LAUNCH = 6
 FA_ERR_ALIGN = 7
+FA_ERR_VARIANT = 8
 
-EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_strerror", "fa_check_args", "fa_bwd_check_args")
+EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_bwd", "fa_strerror", "fa_check_args", "fa_check_args_ex",
+            "fa_bwd_check_args")
 
 _lib = None
 
@@ -60,6 +63,10 @@ def load_library(path=None):
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i]
     lib.fa_check_args.restype = i
+    lib.fa_fwd_ex.argtypes = [vp] * 5 + [i, i, i, i, i, i, f, i, i, i, vp]
+    lib.fa_fwd_ex.restype = i
+    lib.fa_check_args_ex.argtypes = [vp] * 5 + [i, i, i, i, i, i, f, i, i, i]
+    lib.fa_check_args_ex.restype = i
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_check_args.argtypes = [vp] * 10 + [i, i, i, i, f, i]
@@ -96,6 +103,19 @@ def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
     """C ``fa_fwd_f32``: fp32 q, k, v, o and lse; returns the status code."""
     return load_library().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                                      int(N), int(d), float(scale), int(causal), _stream(stream))
+
+
+def fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window, stream=None):
+    """C ``fa_fwd_ex``: bf16 q, o [B, Hq, T, d], k, v [B, Hkv, S, d], fp32 lse."""
+    return load_library().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq), int(Hkv),
+                                    int(T), int(S), int(d), float(scale), int(causal), int(offset), int(window),
+                                    _stream(stream))
+
+
+def fa_check_args_ex(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window):
+    return load_library().fa_check_args_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq),
+                                           int(Hkv), int(T), int(S), int(d), float(scale), int(causal),
+                                           int(offset), int(window))
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale, causal, stream=None):
@@ -185,3 +205,36 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv, delta
+
+
+def forward_ex(q, k, v, causal=False, scale=None, offset=None, window=0, stream=None):
+    """Variants of ``forward`` through ``fa_fwd_ex``: q [B, Hq, T, d] and
+    k, v [B, Hkv, S, d] bfloat16 CUDA tensors (Hq a multiple of Hkv); query
+    row i sits at position offset + i (default S - T) for the causal mask;
+    window > 0 limits each row to the window keys ending at its position.
+    Returns (O [B, Hq, T, d], LSE [B, Hq, T])."""
+    import math
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, T, d] and k, v one [B, Hkv, S, d] shape")
+    if q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+        raise ValueError("q, k and v must share B and d")
+    if any(x.dtype != torch.bfloat16 for x in (q, k, v)):
+        raise ValueError("fa_fwd_ex takes bfloat16 tensors")
+    B, Hq, T, d = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    q, k, v = (x.contiguous() for x in (q, k, v))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if offset is None:
+        offset = S - T
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = fa_fwd_ex(q, k, v, out, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window, stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_ex")
+    return out, lse
+

@@ -283,25 +283,42 @@ __device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& l
 // EXACT = false (fast kernel): the first tile (FIRST) sets the reference to
 // its row max; later tiles compute no max at all and return true in a lane
 // whose weights of this tile sum to more than 2^kSlack (which every weight
-// above 2^kSlack, or an overflow to +inf, implies).
+// above 2^kSlack, or an overflow to +inf, implies).  MAXALL (the variants'
+// kernel): every tile computes its row max, and the reference is the max
+// of the first tile in which the row sees a key; MASK then also applies the
+// sliding window's lower bound when wnd > 0.
 // EXACT = true (recompute kernel): m is the running max and l and acc are
 // rescaled by exp2(m_old - m_new) on every tile.
-template <class C, bool CAUSAL, bool MASK, bool EXACT, bool FIRST>
+template <class C, bool CAUSAL, bool MASK, bool EXACT, bool FIRST, bool MAXALL = false>
 __device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB],
-                                             float& m, float& lsum, int k0, int qw0, int N, float c, int lane) {
+                                             float& m, float& lsum, int k0, int qw0, int N, float c, int lane,
+                                             int wnd = 0) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
   // register i of block sb holds key k0 + 32*sb + 8*(i/4) + 4h + i%4
   if (MASK) {
-    const int query = qw0 + l32;
+    const int query = qw0 + l32;  // the query's position
     const int lim = (CAUSAL ? min(query, N - 1) : N - 1) - (k0 + 4 * h);
+    if (MAXALL && wnd > 0) {
+      // sliding window: keys query - wnd + 1 .. query
+      const int low = query - wnd + 1 - (k0 + 4 * h);
 #pragma unroll
-    for (int sb = 0; sb < C::SB; ++sb)
+      for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        s[sb][i] = (32 * sb + 8 * (i >> 2) + (i & 3) <= lim) ? s[sb][i] : -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int rel = 32 * sb + 8 * (i >> 2) + (i & 3);
+          s[sb][i] = (rel <= lim && rel >= low) ? s[sb][i] : -INFINITY;
+        }
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[sb][i] = (32 * sb + 8 * (i >> 2) + (i & 3) <= lim) ? s[sb][i] : -INFINITY;
+    }
   }
-  if (EXACT || FIRST) {
+  bool had_ref = true;  // the fixed reference was set before this tile
+  if (EXACT || FIRST || MAXALL) {
     // row max: four independent max chains over this half's keys, then the
     // two halves of the wave
     float mq[4];
@@ -324,12 +341,15 @@ __device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
       m = m_new;
     } else {
-      m = mxs;
+      // the reference is the max of the first tile with a visible key
+      had_ref = m != -INFINITY;
+      m = had_ref ? m : mxs;
     }
   }
   // safe reference; after the first tile of the fast kernel m is the finite
-  // max of a tile that holds a visible key of every row (key 0)
-  const float mref = (EXACT || FIRST) ? ((m == -INFINITY) ? 0.f : m) : m;
+  // max of a tile that holds a visible key of every row (key 0), except
+  // with a window (MAXALL), where a row may see its first key later
+  const float mref = (EXACT || FIRST || MAXALL) ? ((m == -INFINITY) ? 0.f : m) : m;
 
   // P = exp2(S*c - m_ref); masked scores give exp2(-inf) = 0
   float sq[4];
@@ -355,18 +375,26 @@ __device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
     for (int db = 0; db < C::DB; ++db) pin(acc[db]);
   }
   // NaN-safe: a NaN sum (NaN inputs) is not flagged
-  return !EXACT && !FIRST && ts > kJumpSum;
+  return !EXACT && !FIRST && had_ref && ts > kJumpSum;
 }
+
+// Arguments of the variants (EXT = true): query rows T and key rows S per
+// head, Hq query heads of which each group of `group` reads one K/V head,
+// the position of query row 0 (causal), a sliding window (0: none) and
+// whether work units pair a heavy and a light query tile.
+struct ExtArgs {
+  int T, S, Hq, group, offset, window, pair;
+};
 
 // EXACT = false: the fast kernel over every query tile.  EXACT = true: the
 // recompute kernel, which only redoes the query rows the fast kernel marked
 // (NaN LSE) and is a no-op for tiles without a marked row.
-template <class C, bool CAUSAL, bool EXACT>
+template <class C, bool CAUSAL, bool EXACT, bool EXT = false>
 __global__ void __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
                    int N, int T_r, int units_per_head, int num_units, int per_xcd, float c,
-                   unsigned int qsign) {
+                   unsigned int qsign, ExtArgs ex) {
   // the K/V ring, then one flag per wave (recompute kernel)
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDSB + 4 * C::NW];
   int LDS_AS* wave_marked = (int LDS_AS*)(smem + C::LDSB);
@@ -384,7 +412,10 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int ur = u - bh * units_per_head;
   int tiles[2];
   int ntiles = 1;
-  if (CAUSAL) {
+  // EXT: T query rows and S key rows per head; otherwise both are N
+  const int Nq = EXT ? ex.T : N;
+  const int Nk = EXT ? ex.S : N;
+  if (CAUSAL && (!EXT || ex.pair)) {
     tiles[0] = T_r - 1 - ur;  // heavy tile first
     tiles[1] = ur;
     ntiles = (tiles[1] < tiles[0]) ? 2 : 1;
@@ -396,20 +427,32 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   LaneOffsets<C> lo;
   lane_offsets<C>(lo, (unsigned)(uintptr_t)(const unsigned char LDS_AS*)smem, w, lane);
 
-  const size_t hoff = (size_t)bh * (size_t)N * C::D;
+  const size_t hoff = (size_t)bh * (size_t)Nq * C::D;
+  // EXT: query head h of batch b reads K/V head h / group (the index is
+  // wave-uniform; readfirstlane keeps the addresses derived from it scalar)
+  size_t kvoff = hoff;
+  if (EXT) {
+    const unsigned kvh = (unsigned)__builtin_amdgcn_readfirstlane(
+        (bh / ex.Hq) * (ex.Hq / ex.group) + (bh % ex.Hq) / ex.group);
+    kvoff = (size_t)kvh * (size_t)Nk * C::D;
+  }
   const uint16_t* qh = q + hoff;
-  const uint16_t* kh = k + hoff;
-  const uint16_t* vh = v + hoff;
+  const uint16_t* kh = k + kvoff;
+  const uint16_t* vh = v + kvoff;
+  const int qoff = (EXT && CAUSAL) ? ex.offset : 0;   // position of query row 0
+  const int wnd = (EXT && CAUSAL) ? ex.window : 0;    // sliding window (0: none)
 
   for (int ti = 0; ti < ntiles; ++ti) {
-    const int q0 = tiles[ti] * C::BR;
+    // (EXT: said to be wave-uniform, so that the addresses derived from it
+    // stay scalar)
+    const int q0 = EXT ? __builtin_amdgcn_readfirstlane(tiles[ti] * C::BR) : tiles[ti] * C::BR;
     const int qw0 = q0 + w * 32;
 
     bool mine = false;  // recompute kernel: this lane's row was marked
     if (EXACT) {
       const int query = qw0 + l32;
-      if (query < N) {
-        const float x = lse[(size_t)bh * N + query];
+      if (query < Nq) {
+        const float x = lse[(size_t)bh * Nq + query];
         mine = x != x;
       }
       if (lane == 0) wave_marked[w] = __builtin_amdgcn_ballot_w64(mine) != 0;
@@ -425,7 +468,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // dims 16*kb + 8*(l/32) .. +7.  Rows past N are clamped (never stored).
     bf16x8 qr[C::KB];
     {
-      const int row = min(qw0 + l32, N - 1);
+      const int row = min(qw0 + l32, Nq - 1);
       const uint16_t* src = qh + (size_t)row * C::D + 8 * h;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
@@ -435,11 +478,15 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       }
     }
 
-    const int kv_end = CAUSAL ? min(N, q0 + C::BR) : N;
-    const int nkv = (kv_end + C::BC - 1) / C::BC;
-    // leading tiles that need no mask for any query of the workgroup
+    const int kv_end = CAUSAL ? min(Nk, qoff + q0 + C::BR) : Nk;
+    // EXT with a window: the first key tile any query of the tile can see
+    const int kt0 = (EXT && wnd > 0) ? __builtin_amdgcn_readfirstlane(max(0, qoff + q0 - wnd + 1) / C::BC) : 0;
+    const int nkv = (kv_end + C::BC - 1) / C::BC - kt0;  // key tiles kt0 .. kt0 + nkv - 1
+    // leading tiles that need no mask for any query of the workgroup (EXT:
+    // every tile goes through the masked path)
     int nfull = min(nkv, N / C::BC);
     if (CAUSAL) nfull = min(nfull, (q0 + 1) / C::BC);
+    if (EXT) nfull = 0;
 
     float m = -INFINITY, lsum = 0.f;
     f32x16 acc[C::DB];
@@ -483,10 +530,10 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     bf16x8 kpre[C::KD][C::SB];
     // M(j) (HAS_QK: K_j at stage offset kst; HAS_PV: V_{j-1} at vst); !VCOPY:
     // copies for tile j+2 into stage offset dst
-    auto mphase = [&](int j, int kst, int vst, int dst, auto has_qk, auto has_pv) {
+    auto mphase = [&](int j, int kst, int vst, int dst, auto has_qk, auto has_pv) __attribute__((always_inline)) {
       constexpr bool QK = decltype(has_qk)::value, PV = decltype(has_pv)::value;
       if (!VC) {
-        if (j + 2 < nkv) load_tile<C>(msrc, mdst + dst, (j + 2) * C::BC, N, lo, w);
+        if (j + 2 < nkv) load_tile<C>(msrc, mdst + dst, (kt0 + j + 2) * C::BC, Nk, lo, w);
         if (QK) prefetch_k<C>(kpre, lo, kst);
       }
       tile_m<C, QK, PV>(kst, vst, lo, qr, s, p, acc, kpre);
@@ -503,14 +550,15 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     };
     // V(j): softmax of tile j; VCOPY: copies for tile j+3 into stage offset
     // dst, then read ahead K of tile j+1 at stage offset kst1
-    auto vphase = [&](int j, int dst, int kst1, auto mask_tag, auto first_tag) {
+    auto vphase = [&](int j, int dst, int kst1, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
       constexpr bool FIRST = decltype(first_tag)::value;
-      jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST>(s, p, acc, m, lsum, j * C::BC, qw0, N, c, lane);
+      jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, EXT>(s, p, acc, m, lsum, (kt0 + j) * C::BC, qoff + qw0,
+                                                                 Nk, c, lane, wnd);
       __builtin_amdgcn_sched_barrier(0);
       if (VC) {
         if (j + 3 < nkv) {
-          load_tile<C>(msrc, mdst + dst, (j + 3) * C::BC, N, lo, w);
+          load_tile<C>(msrc, mdst + dst, (kt0 + j + 3) * C::BC, Nk, lo, w);
           wait_copies<C::NI>();
         } else {
           wait_copies<0>();
@@ -523,13 +571,13 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     };
     // one step; stages of tiles j, j-1, j+AHEAD, j+1 (compile-time constants
     // in the unrolled loop, run-time values otherwise)
-    auto step = [&](int j, int kst, int vst, int dst, int kst1, auto mask_tag) {
+    auto step = [&](int j, int kst, int vst, int dst, int kst1, auto mask_tag) __attribute__((always_inline)) {
       mphase(j, kst, vst, dst, std::true_type{}, std::true_type{});
       barrier();
       vphase(j, dst, kst1, mask_tag, std::false_type{});
     };
     constexpr int KT = C::KT;
-    auto stg = [](int t) { return (t & 3) * KT; };
+    auto stg = [](int t) __attribute__((always_inline)) { return (t & 3) * KT; };
 
     if constexpr (VC) {
       // One barrier per step.  Between barriers j and j+1 (window j) the
@@ -542,7 +590,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       // waits for V_{j+1}.  So K_t and V_t are complete by barrier t-1, and
       // the first reads of tile t -- the read-ahead of K_t in window t-1 and
       // the leading P V of tile t in window t+1 -- come after it.
-      auto m1 = [&](int kst, int vst, auto has_qk, auto has_pv) {
+      auto m1 = [&](int kst, int vst, auto has_qk, auto has_pv) __attribute__((always_inline)) {
         constexpr bool QK = decltype(has_qk)::value, PV = decltype(has_pv)::value;
         tile_m<C, QK, PV>(kst, vst, lo, qr, s, p, acc, kpre);
 #pragma unroll
@@ -555,15 +603,16 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       };
       // V(j) with the stages of tiles j+1, j+2, j+3 (LAG: this wave is in the
       // lagging half, which copies V; the leading half copies K)
-      auto v1 = [&](int j, int s1, int s2, int s3, auto lag_tag, auto mask_tag, auto first_tag) {
+      auto v1 = [&](int j, int s1, int s2, int s3, auto lag_tag, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
         constexpr bool LAG = decltype(lag_tag)::value;
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool FIRST = decltype(first_tag)::value;
-        jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST>(s, p, acc, m, lsum, j * C::BC, qw0, N, c, lane);
+        jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, EXT>(s, p, acc, m, lsum, (kt0 + j) * C::BC,
+                                                                   qoff + qw0, Nk, c, lane, wnd);
         __builtin_amdgcn_sched_barrier(0);
         const int ct = LAG ? j + 2 : j + 3;  // the tile this wave copies now
         if (ct < nkv) {
-          load_tile<C>(LAG ? vh : kh, lo.base + (LAG ? C::VBASE + s2 : s3), ct * C::BC, N, lo, w);
+          load_tile<C>(LAG ? vh : kh, lo.base + (LAG ? C::VBASE + s2 : s3), (kt0 + ct) * C::BC, Nk, lo, w);
           wait_copies<C::NI>();
         } else {
           wait_copies<0>();
@@ -575,12 +624,12 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       };
       // the whole key loop of one half (each half gets its own copy of the
       // code, so that the register allocation follows its own phase order)
-      auto run = [&](auto lag_tag) {
+      auto run = [&](auto lag_tag) __attribute__((always_inline)) {
         constexpr bool LAG = decltype(lag_tag)::value;
         const std::true_type T{};
         const std::false_type F{};
         // window j for 1 <= j < nkv - 1, stages of tiles j-1 .. j+3
-        auto window = [&](int j, int sm1, int s0, int s1, int s2, int s3, auto mask_tag) {
+        auto window = [&](int j, int sm1, int s0, int s1, int s2, int s3, auto mask_tag) __attribute__((always_inline)) {
           if (!LAG) {
             v1(j, s1, s2, s3, lag_tag, mask_tag, F);
             m1(s1, s0, T, T);
@@ -591,7 +640,8 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           barrier();
         };
         for (int t = 0; t < (LAG ? 2 : 3); ++t)
-          if (t < nkv) load_tile<C>(LAG ? vh : kh, lo.base + (LAG ? C::VBASE : 0) + stg(t), t * C::BC, N, lo, w);
+          if (t < nkv)
+            load_tile<C>(LAG ? vh : kh, lo.base + (LAG ? C::VBASE : 0) + stg(t), (kt0 + t) * C::BC, Nk, lo, w);
         wait_copies<0>();
         barrier();
         prefetch_k<C>(kpre, lo, 0);
@@ -644,7 +694,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     } else {
 
       for (int t = 0; t < AHEAD; ++t)
-        if (t < nkv) load_tile<C>(msrc, mdst + stg(t), t * C::BC, N, lo, w);
+        if (t < nkv) load_tile<C>(msrc, mdst + stg(t), (kt0 + t) * C::BC, Nk, lo, w);
       wait_copies<0>();
       barrier();
       if (lag) barrier();
@@ -682,7 +732,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     jumped = half_max(jumped ? 1.f : 0.f) != 0.f;
     const float inv = 1.f / lt;
     const int query = qw0 + l32;
-    if (query < N && (!EXACT || mine)) {  // the recompute kernel stores only marked rows
+    if (query < Nq && (!EXACT || mine)) {  // the recompute kernel stores only marked rows
       uint16_t* orow = o + hoff + (size_t)query * C::D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -695,7 +745,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
       // a row whose scores jumped past the fixed reference is marked (NaN
       // LSE) for the recompute kernel
-      if (h == 0) lse[(size_t)bh * N + query] = jumped ? __builtin_nanf("") : (m + __log2f(lt)) * kLn2;
+      if (h == 0) lse[(size_t)bh * Nq + query] = jumped ? __builtin_nanf("") : (m + __log2f(lt)) * kLn2;
     }
   }
 }
@@ -810,13 +860,58 @@ void launch_bf16(const void* q, const void* k, const void* v, void* o, float* ls
   const int grid = per_xcd * 8;
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, false>), dim3(grid), dim3(C::NW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, T_r,
-                     units_per_head, num_units, per_xcd, c, qsign);
+                     units_per_head, num_units, per_xcd, c, qsign, ExtArgs{});
   // Waves marked by the fast kernel are redone with exact rescaling; the
   // launch is ordered after the fast kernel on the stream and its
   // workgroups exit at once when nothing is marked.
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, true>), dim3(grid), dim3(C::NW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, T_r,
-                     units_per_head, num_units, per_xcd, c, qsign);
+                     units_per_head, num_units, per_xcd, c, qsign, ExtArgs{});
+}
+
+template <class C, bool CAUSAL>
+void launch_bf16_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                    int T, int S, int offset, int window, float c, unsigned qsign, hipStream_t stream) {
+  const int T_r = (T + C::BR - 1) / C::BR;
+  // with a window every query tile costs about the same: no pairing
+  const int pair = CAUSAL && window == 0;
+  const int units_per_head = pair ? (T_r + 1) / 2 : T_r;
+  const int num_units = B * Hq * units_per_head;
+  const int per_xcd = (num_units + 7) / 8;
+  const int grid = per_xcd * 8;
+  const ExtArgs ex{T, S, Hq, Hq / Hkv, offset, window, pair};
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, false, true>), dim3(grid), dim3(C::NW * 64), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, T, T_r,
+                     units_per_head, num_units, per_xcd, c, qsign, ex);
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, true, true>), dim3(grid), dim3(C::NW * 64), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, T, T_r,
+                     units_per_head, num_units, per_xcd, c, qsign, ex);
+}
+
+int check_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int Hq,
+             int Hkv, int T, int S, int d, float scale, int causal, int offset, int window) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || T < 0 || S < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const long long rows = (long long)B * Hq * T;
+  if (rows == 0) return FA_OK;
+  if (Hkv == 0 || Hq % Hkv != 0) return FA_ERR_VARIANT;
+  if (S == 0) return FA_ERR_VARIANT;  // a query row would see no key
+  if (window < 0 || (window > 0 && !causal)) return FA_ERR_VARIANT;
+  if (causal && (offset < 0 || offset > S - T)) return FA_ERR_VARIANT;
+  const long long krows = (long long)B * Hkv * S;
+  if ((long long)B * Hq > (1LL << 30) || rows > (1LL << 40) || krows > (1LL << 40)) return FA_ERR_SHAPE;
+  if ((long long)B * Hq * ((T + 31) / 32) > (1LL << 30)) return FA_ERR_SHAPE;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
+  if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
+  const size_t qb = (size_t)rows * d * 2;
+  const size_t kb = (size_t)krows * d * 2;
+  const size_t lb = (size_t)rows * sizeof(float);
+  if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb) || overlaps(lse, lb, q, qb) ||
+      overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, kb) || overlaps(lse, lb, o, qb))
+    return FA_ERR_ALIAS;
+  return FA_OK;
 }
 
 template <int D, bool CAUSAL>
@@ -882,6 +977,32 @@ extern "C" int fa_fwd_f32(const float* q, const float* k, const float* v, float*
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+extern "C" int fa_check_args_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                int B, int Hq, int Hkv, int T, int S, int d, float scale, int causal, int offset,
+                                int window) {
+  return check_ex(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window);
+}
+
+extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                         int T, int S, int d, float scale, int causal, int offset, int window,
+                         hipStream_t stream) {
+  const int st = check_ex(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window);
+  if (st != FA_OK) return st;
+  if ((long long)B * Hq * T == 0) return FA_OK;
+  const unsigned qsign = (scale < 0.f) ? 0x80008000u : 0u;  // as in fa_fwd
+  const float c = scale == 0.f ? 0x1p-100f : fabsf(scale) * kLog2e;
+  const int off = causal ? offset : 0;
+  const int wnd = causal ? window : 0;
+  if (d == 128) {
+    if (causal) launch_bf16_ex<CfgD128, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream);
+    else launch_bf16_ex<CfgD128, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream);
+  } else {
+    if (causal) launch_bf16_ex<CfgD64, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream);
+    else launch_bf16_ex<CfgD64, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream);
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 extern "C" const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -892,6 +1013,7 @@ extern "C" const char* fa_strerror(int status) {
     case FA_ERR_ALIAS: return "output buffers overlap inputs or each other";
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
     case FA_ERR_ALIGN: return "pointer not aligned (16 bytes for q/k/v/o, 4 for lse)";
+    case FA_ERR_VARIANT: return "inconsistent heads, offset or window (fa_fwd_ex)";
     default: return "unknown status";
   }
 }

@@ -24,8 +24,8 @@ def declared_functions():
 
 
 def test_header_declares_the_abi():
-    assert declared_functions() == sorted(["fa_bwd", "fa_bwd_check_args", "fa_check_args", "fa_fwd",
-                                           "fa_fwd_f32", "fa_strerror"])
+    assert declared_functions() == sorted(["fa_bwd", "fa_bwd_check_args", "fa_check_args", "fa_check_args_ex",
+                                           "fa_fwd", "fa_fwd_ex", "fa_fwd_f32", "fa_strerror"])
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -38,7 +38,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_strerror_covers_codes():
-    for code in range(0, 8):
+    for code in range(0, 9):
         s = fa.fa_strerror(code)
         assert s and s != "unknown status", code
     assert fa.fa_strerror(99) == "unknown status"
@@ -140,4 +140,39 @@ def test_backward_refuses_cpu_tensors():
     lse = torch.zeros(1, 1, 4)
     with pytest.raises(ValueError):
         fa.backward(x, x, x, x, lse, x)
+
+
+def _ex(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, Hq=8, Hkv=2, T=100, S=400, d=128, scale=0.1, causal=1, offset=300,
+             window=0)
+    a.update(kw)
+    return fa.fa_check_args_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["T"], a["S"],
+                               a["d"], a["scale"], a["causal"], a["offset"], a["window"])
+
+
+def test_ex_check_args_ok():
+    assert _ex() == fa.FA_OK
+    assert _ex(window=64) == fa.FA_OK
+    assert _ex(causal=0, offset=-5, T=1000, S=3) == fa.FA_OK   # cross-attention: offset ignored
+    assert _ex(T=1, offset=399) == fa.FA_OK                    # decode
+    assert _ex(B=0, q=None) == fa.FA_OK                        # empty
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Hkv=3), fa.FA_ERR_VARIANT),            # 8 query heads over 3 KV heads
+    (dict(Hkv=0), fa.FA_ERR_VARIANT),
+    (dict(S=0), fa.FA_ERR_VARIANT),
+    (dict(offset=301), fa.FA_ERR_VARIANT),       # > S - T
+    (dict(offset=-1), fa.FA_ERR_VARIANT),
+    (dict(T=500, offset=0), fa.FA_ERR_VARIANT),  # T > S with the causal mask
+    (dict(window=-1), fa.FA_ERR_VARIANT),
+    (dict(window=8, causal=0), fa.FA_ERR_VARIANT),
+    (dict(d=96), fa.FA_ERR_HEAD_DIM),
+    (dict(T=-1), fa.FA_ERR_SHAPE),
+    (dict(k=None), fa.FA_ERR_NULL),
+    (dict(o=K), fa.FA_ERR_ALIAS),
+    (dict(lse=O + 128), fa.FA_ERR_ALIAS),
+])
+def test_ex_check_args_errors(kw, code):
+    assert _ex(**kw) == code
 
