@@ -28,6 +28,9 @@ measured HBM bytes of each shape (one dispatch of the main kernel per step).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--backward]
        python bench.py --shapes "1,64,4096,128,1;1,64,8192,64,0" [--steps K] [--warmup W]
+A shape may add ",Hkv,window[,T]" to run fa_fwd_ex instead: Hkv K/V heads,
+a sliding window (0: none) and T query rows at the newest positions of the
+N keys (default T = N); FLOPs then count the visible (query, key) pairs.
 """
 
 import argparse
@@ -202,17 +205,26 @@ def shape_sweep(args):
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     for spec in args.shapes.split(";"):
-        B, H, N, d, causal = (int(x) for x in spec.split(","))
+        f = [int(x) for x in spec.split(",")]
+        B, H, N, d, causal = f[:5]
+        ext = len(f) > 5
+        hkv, window = (f[5], f[6]) if ext else (H, 0)
+        T = f[7] if len(f) > 7 else N
         q, k, v = workloads.make_qkv(B, H, N, d, torch.bfloat16, 1000 + N + d)
-        qd, kd, vd = (x.to(dev) for x in (q, k, v))
+        qd = q[:, :, N - T:].contiguous().to(dev)
+        kd, vd = (x[:, :hkv].contiguous().to(dev) for x in (k, v))
         o = torch.empty_like(qd)
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
         scale = 1.0 / math.sqrt(d)
 
         def step():
-            st = fa.fa_fwd(qd, kd, vd, o, lse, B, H, N, d, scale, causal, stream.cuda_stream)
+            if ext:
+                st = fa.fa_fwd_ex(qd, kd, vd, o, lse, B, H, hkv, T, N, d, scale, causal, N - T, window,
+                                  stream.cuda_stream)
+            else:
+                st = fa.fa_fwd(qd, kd, vd, o, lse, B, H, N, d, scale, causal, stream.cuda_stream)
             if st != fa.FA_OK:
-                raise fa.FaError(st, "fa_fwd")
+                raise fa.FaError(st, "fa_fwd_ex" if ext else "fa_fwd")
 
         for _ in range(args.warmup):
             step()
@@ -224,9 +236,17 @@ def shape_sweep(args):
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
-        flops = 4.0 * B * H * N * N * d / (2 if causal else 1)
+        if ext:
+            # visible (query, key) pairs: row i (position N - T + i) sees
+            # min(position + 1, window or position + 1) keys when causal
+            pos = [N - T + i for i in range(T)]
+            pairs = sum(min(p + 1, window) if window else p + 1 for p in pos) if causal else T * N
+            flops = 4.0 * B * H * pairs * d
+        else:
+            flops = 4.0 * B * H * N * N * d / (2 if causal else 1)
         br, bc = 256, (64 if d == 128 else 128)
-        print(json.dumps({"shape": {"B": B, "H": H, "N": N, "d": d, "causal": bool(causal)},
+        print(json.dumps({"shape": {"B": B, "H": H, "N": N, "d": d, "causal": bool(causal), "Hkv": hkv,
+                                    "window": window, "T": T, "entry": "fa_fwd_ex" if ext else "fa_fwd"},
                           "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
                           "once_bytes": workloads.hbm_once_bytes(B, H, N, d),
                           "stream_bytes": workloads.tile_stream_bytes(B, H, N, d, br, bc, bool(causal)),

@@ -482,11 +482,21 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     // EXT with a window: the first key tile any query of the tile can see
     const int kt0 = (EXT && wnd > 0) ? __builtin_amdgcn_readfirstlane(max(0, qoff + q0 - wnd + 1) / C::BC) : 0;
     const int nkv = (kv_end + C::BC - 1) / C::BC - kt0;  // key tiles kt0 .. kt0 + nkv - 1
-    // leading tiles that need no mask for any query of the workgroup (EXT:
-    // every tile goes through the masked path)
+    // leading tiles that need no mask for any query of the workgroup
     int nfull = min(nkv, N / C::BC);
     if (CAUSAL) nfull = min(nfull, (q0 + 1) / C::BC);
-    if (EXT) nfull = 0;
+    // tiles 1 .. jhead-1 are masked too (EXT: the window's left edge)
+    int jhead = 1;
+    if (EXT) {
+      // unmasked: the tile lies below S and at or below every row's
+      // position, and (window) after the tile holding the latest row's
+      // first visible key, so that every row has set its reference before
+      const int glast = min(Nk / C::BC, CAUSAL ? (qoff + q0 + 1) / C::BC : Nk / C::BC);
+      const int gfirst = wnd > 0 ? max(0, qoff + q0 + C::BR - wnd) / C::BC + 1 : 1;
+      nfull = max(0, glast - kt0);
+      const int jh = max(1, gfirst - kt0);
+      jhead = jh + ((1 - jh) & 3);  // the first j >= jh with j % 4 == 1 (unrolled stage order)
+    }
 
     float m = -INFINITY, lsum = 0.f;
     f32x16 acc[C::DB];
@@ -553,7 +563,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     auto vphase = [&](int j, int dst, int kst1, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
       constexpr bool FIRST = decltype(first_tag)::value;
-      jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, EXT>(s, p, acc, m, lsum, (kt0 + j) * C::BC, qoff + qw0,
+      jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, EXT && MASK>(s, p, acc, m, lsum, (kt0 + j) * C::BC, qoff + qw0,
                                                                  Nk, c, lane, wnd);
       __builtin_amdgcn_sched_barrier(0);
       if (VC) {
@@ -607,7 +617,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         constexpr bool LAG = decltype(lag_tag)::value;
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool FIRST = decltype(first_tag)::value;
-        jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, EXT>(s, p, acc, m, lsum, (kt0 + j) * C::BC,
+        jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, EXT && MASK>(s, p, acc, m, lsum, (kt0 + j) * C::BC,
                                                                    qoff + qw0, Nk, c, lane, wnd);
         __builtin_amdgcn_sched_barrier(0);
         const int ct = LAG ? j + 2 : j + 3;  // the tile this wave copies now
@@ -662,6 +672,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         // every stage offset is a compile-time constant
         const int j1 = max(1, min(nfull, nkv - 1));
         int j = 1;
+        for (; j < min(jhead, j1); ++j) window(j, stg(j - 1), stg(j), stg(j + 1), stg(j + 2), stg(j + 3), T);
         for (; j + 3 < j1; j += 4) {
           window(j + 0, stg(0), stg(1), stg(2), stg(3), stg(4), F);
           window(j + 1, stg(1), stg(2), stg(3), stg(4), stg(5), F);
@@ -703,12 +714,15 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       if (VC) prefetch_k<C>(kpre, lo, 0);
       mphase(0, 0, 0, stg(AHEAD), std::true_type{}, std::false_type{});
       barrier();
-      if (nfull > 0) vphase(0, stg(AHEAD), stg(1), std::false_type{}, std::true_type{});
+      // (EXT: the first tile may be the window's left edge: always masked)
+      if (nfull > 0 && !EXT) vphase(0, stg(AHEAD), stg(1), std::false_type{}, std::true_type{});
       else vphase(0, stg(AHEAD), stg(1), std::true_type{}, std::true_type{});
       // unmasked steps 1 .. j1-1, unrolled by the ring size so that every
       // stage offset is a compile-time constant (step j uses stage j % 4)
       const int j1 = max(1, min(nfull, nkv));
       int j = 1;
+      for (; j < min(jhead, j1); ++j)
+        step(j, stg(j), stg(j - 1), stg(j + AHEAD), stg(j + 1), std::true_type{});
       for (; j + 3 < j1; j += 4) {
         step(j + 0, stg(1), stg(0), stg(1 + AHEAD), stg(2), std::false_type{});
         step(j + 1, stg(2), stg(1), stg(2 + AHEAD), stg(3), std::false_type{});
