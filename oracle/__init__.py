@@ -11,12 +11,14 @@ its Python binding never do, and the oracle never imports them.
                 definition and in the recomputation form (P from the saved
                 LSE, D = O . dO).
   * ``variants`` - grouped K/V heads, queries at an offset into a longer
-                key sequence, and a sliding window.
+                key sequence, a sliding window, and split-KV partials with
+                their merge.
 """
 
 from .ref import as_f64, scores_ref, probabilities_ref, attention_ref, attention_rows_ref
 from .tiled import tiled_ref
-from .variants import attention_ex_ref, attention_ex_rows_ref, visible_mask
+from .variants import (attention_ex_ref, attention_ex_rows_ref, attention_split_ref, merge_mla_ref,
+                       merge_partials_ref, visible_mask)
 from .backward import (attention_bwd_ref, attention_bwd_from_lse_ref, attention_bwd_rows_ref,
                        attention_bwd_cols_ref)
 
@@ -24,5 +26,5 @@ __all__ = [
     "as_f64", "scores_ref", "probabilities_ref", "attention_ref",
     "attention_rows_ref", "tiled_ref", "attention_bwd_ref", "attention_bwd_from_lse_ref",
     "attention_bwd_rows_ref", "attention_bwd_cols_ref", "attention_ex_ref", "attention_ex_rows_ref",
-    "visible_mask",
+    "visible_mask", "attention_split_ref", "merge_partials_ref", "merge_mla_ref",
 ]

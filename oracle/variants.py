@@ -15,6 +15,9 @@ j >= p_i - W + 1.  Then, with the score matrix materialised,
 S = scale * q k^T (masked to -inf), O = softmax(S) v and
 LSE = logsumexp(S) per row.
 
+Split-KV (flash-decoding): ``attention_split_ref`` computes the partial
+result of each key chunk and ``merge_partials_ref`` combines them.
+
 Sources (the pages this follows): "15. FlashAttention"
 (inference.shantanugoel.com), section "The kernel" (query head h reads KV
 head h // group; query row i at absolute position offset + i with default
@@ -110,4 +113,64 @@ def attention_ex_rows_ref(q, k, v, scale, causal, offset, window, rows):
         e = np.exp(s - m)
         o[r] = (e @ v[lo:hi]) / e.sum()
         lse[r] = m + np.log(e.sum())
+    return o, lse
+
+
+def merge_partials_ref(o_parts, lse_parts):
+    """Merge partial results of disjoint key chunks: with O_g the softmax
+    output over chunk g alone and L_g its log-sum-exp (-inf for a chunk
+    with no visible key, whose O_g is ignored),
+        L = log sum_g exp(L_g),   O = sum_g exp(L_g - L) O_g.
+    ("15. FlashAttention", section "Decode is different: flash-decoding":
+    the (m, l, a) merge rule, here in its (O, L) form.)  Arrays are
+    [splits, ..., d] and [splits, ...]."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    w = np.exp(lse_parts - m[None])  # exp(-inf) = 0 for empty chunks
+    tot = w.sum(axis=0)
+    o = np.einsum("g...,g...d->...d", w, np.where(np.isfinite(lse_parts)[..., None], o_parts, 0.0))
+    return o / tot[..., None], m + np.log(tot)
+
+
+def merge_mla_ref(parts):
+    """The same merge in the pages' (m, l, a) form: m = max m_g,
+    l = sum e^{m_g - m} l_g, a = sum e^{m_g - m} a_g, O = a / l.  ``parts``
+    is a list of (m [...], l [...], a [..., d])."""
+    m = np.max([p[0] for p in parts], axis=0)
+    l = sum(np.exp(p[0] - m) * p[1] for p in parts)
+    a = sum(np.exp(p[0] - m)[..., None] * p[2] for p in parts)
+    return a / l[..., None], m + np.log(l)
+
+
+def attention_split_ref(q, k, v, scale, causal, offset=None, window=0, chunk=None):
+    """Partial (O_g, L_g) of every key chunk of ``chunk`` keys, each from the
+    definition over the keys of its chunk that a row sees (O_g = 0 and
+    L_g = -inf where it sees none); returns (O_parts [G, B, Hq, T, d],
+    LSE_parts [G, B, Hq, T])."""
+    q, k, v = (as_f64(x) for x in (q, k, v))
+    B, hq, T, d = q.shape
+    hkv, S = k.shape[1], k.shape[2]
+    if offset is None:
+        offset = S - T
+    group = hq // hkv
+    vis = visible_mask(T, S, causal, offset, window)
+    G = -(-S // chunk)
+    o = np.zeros((G, B, hq, T, v.shape[-1]))
+    lse = np.full((G, B, hq, T), -np.inf)
+    for g in range(G):
+        c0, c1 = g * chunk, min(S, (g + 1) * chunk)
+        vg = vis[:, c0:c1]
+        rows = vg.any(axis=1)
+        for b in range(B):
+            for h in range(hq):
+                kh, vh = k[b, h // group, c0:c1], v[b, h // group, c0:c1]
+                s = np.where(vg, scale * (q[b, h] @ kh.T), -np.inf)[rows]
+                if s.size == 0:
+                    continue
+                m = s.max(axis=1)
+                e = np.exp(s - m[:, None])
+                l = e.sum(axis=1)
+                o[g, b, h, rows] = (e / l[:, None]) @ vh
+                lse[g, b, h, rows] = m + np.log(l)
     return o, lse

@@ -192,3 +192,49 @@ def test_argument_errors():
         attention_ex_ref(q, k, k, 1.0, False, None, 3)  # window without the causal mask
     with pytest.raises(ValueError):
         attention_ex_ref(q, k, k, 1.0, True, 3, 0)      # offset > S - T
+
+
+# ------------------------------------------------------------ split-KV merge
+from oracle.variants import attention_split_ref, merge_mla_ref, merge_partials_ref  # noqa: E402
+
+
+@pytest.mark.parametrize("causal,off,W,chunk", [(False, None, 0, 7), (True, None, 0, 5), (True, 10, 6, 4),
+                                                (True, 0, 0, 64), (True, None, 3, 1)])
+def test_merge_of_partials_equals_unsplit(causal, off, W, chunk):
+    """Chunked partials merged == the unsplit definition ("15. FlashAttention",
+    "Decode is different: flash-decoding")."""
+    r = _rng(40)
+    B, hq, hkv, T, S, d = 1, 4, 2, 9, 30, 5
+    q = r.standard_normal((B, hq, T, d)); k = r.standard_normal((B, hkv, S, d)); v = r.standard_normal((B, hkv, S, d))
+    op, lp = attention_split_ref(q, k, v, 0.7, causal, off, W, chunk)
+    o, lse = merge_partials_ref(op, lp)
+    o2, lse2 = attention_ex_ref(q, k, v, 0.7, causal, off, W)
+    _close(o, o2, 1e-13, "O"); _close(lse, lse2, 1e-13, "LSE")
+
+
+def test_merge_is_associative_and_matches_the_m_l_a_form():
+    """Any grouping of the partials gives the same result, and the (O, L)
+    form equals the pages' (m, l, a) form."""
+    r = _rng(41)
+    G, n, d = 5, 6, 3
+    m = r.standard_normal((G, n)) * 3
+    l = np.exp(r.standard_normal((G, n)))
+    a = r.standard_normal((G, n, d)) * l[..., None]
+    o_parts, lse_parts = a / l[..., None], m + np.log(l)
+    o, lse = merge_partials_ref(o_parts, lse_parts)
+    o2, lse2 = merge_mla_ref([(m[g], l[g], a[g]) for g in range(G)])
+    _close(o, o2, 1e-13, "O vs (m, l, a)"); _close(lse, lse2, 1e-13, "LSE vs (m, l, a)")
+    oa, la = merge_partials_ref(o_parts[:2], lse_parts[:2])
+    ob, lb = merge_partials_ref(o_parts[2:], lse_parts[2:])
+    o3, lse3 = merge_partials_ref(np.stack([oa, ob]), np.stack([la, lb]))
+    _close(o3, o, 1e-13, "grouped O"); _close(lse3, lse, 1e-13, "grouped LSE")
+
+
+def test_empty_chunk_contributes_nothing():
+    r = _rng(42)
+    o_parts = r.standard_normal((3, 4, 2)); lse_parts = r.standard_normal((3, 4))
+    lse_parts[1] = -np.inf
+    o_parts[1] = np.nan  # never read
+    o, lse = merge_partials_ref(o_parts, lse_parts)
+    o2, lse2 = merge_partials_ref(o_parts[[0, 2]], lse_parts[[0, 2]])
+    _close(o, o2, 1e-15, "O"); _close(lse, lse2, 1e-15, "LSE")
