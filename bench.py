@@ -28,9 +28,12 @@ measured HBM bytes of each shape (one dispatch of the main kernel per step).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--backward]
        python bench.py --shapes "1,64,4096,128,1;1,64,8192,64,0" [--steps K] [--warmup W]
-A shape may add ",Hkv,window[,T]" to run fa_fwd_ex instead: Hkv K/V heads,
-a sliding window (0: none) and T query rows at the newest positions of the
-N keys (default T = N); FLOPs then count the visible (query, key) pairs.
+A shape may add ",Hkv,window[,T[,nsplit]]" to run fa_fwd_ex instead: Hkv K/V
+heads, a sliding window (0: none) and T query rows at the newest positions
+of the N keys (default T = N); FLOPs then count the visible (query, key)
+pairs.  nsplit > 1 runs fa_fwd_split (split-KV with that many key chunks,
+then the merge) instead; kv_gbs is then the K/V bytes read once per step
+over the step time, the bound of decode (T = 1).
 """
 
 import argparse
@@ -210,21 +213,29 @@ def shape_sweep(args):
         ext = len(f) > 5
         hkv, window = (f[5], f[6]) if ext else (H, 0)
         T = f[7] if len(f) > 7 else N
+        nsplit = f[8] if len(f) > 8 else 1
         q, k, v = workloads.make_qkv(B, H, N, d, torch.bfloat16, 1000 + N + d)
         qd = q[:, :, N - T:].contiguous().to(dev)
         kd, vd = (x[:, :hkv].contiguous().to(dev) for x in (k, v))
         o = torch.empty_like(qd)
         lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
         scale = 1.0 / math.sqrt(d)
+        G = fa.fa_split_chunks(N, nsplit)
+        ws_o = torch.empty((G, B, H, T, d), dtype=torch.float32, device=dev) if nsplit > 1 else None
+        ws_l = torch.empty((G, B, H, T), dtype=torch.float32, device=dev) if nsplit > 1 else None
+        entry = "fa_fwd_split" if nsplit > 1 else ("fa_fwd_ex" if ext else "fa_fwd")
 
         def step():
-            if ext:
+            if nsplit > 1:
+                st = fa.fa_fwd_split(qd, kd, vd, o, lse, B, H, hkv, T, N, d, scale, causal, N - T, window, nsplit,
+                                     ws_o, ws_l, stream.cuda_stream)
+            elif ext:
                 st = fa.fa_fwd_ex(qd, kd, vd, o, lse, B, H, hkv, T, N, d, scale, causal, N - T, window,
                                   stream.cuda_stream)
             else:
                 st = fa.fa_fwd(qd, kd, vd, o, lse, B, H, N, d, scale, causal, stream.cuda_stream)
             if st != fa.FA_OK:
-                raise fa.FaError(st, "fa_fwd_ex" if ext else "fa_fwd")
+                raise fa.FaError(st, entry)
 
         for _ in range(args.warmup):
             step()
@@ -246,12 +257,13 @@ def shape_sweep(args):
             flops = 4.0 * B * H * N * N * d / (2 if causal else 1)
         br, bc = 256, (64 if d == 128 else 128)
         print(json.dumps({"shape": {"B": B, "H": H, "N": N, "d": d, "causal": bool(causal), "Hkv": hkv,
-                                    "window": window, "T": T, "entry": "fa_fwd_ex" if ext else "fa_fwd"},
+                                    "window": window, "T": T, "entry": entry, "nsplit": nsplit, "chunks": G},
                           "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                          "kv_gbs": round(2.0 * B * hkv * N * d * 2 / ms / 1e6, 1),
                           "once_bytes": workloads.hbm_once_bytes(B, H, N, d),
                           "stream_bytes": workloads.tile_stream_bytes(B, H, N, d, br, bc, bool(causal)),
                           "tile": {"Br": br, "Bc": bc}}), flush=True)
-        del qd, kd, vd, o, lse
+        del qd, kd, vd, o, lse, ws_o, ws_l
 
 
 def main():

@@ -66,7 +66,7 @@ enum fa_status {
     FA_ERR_ALIAS = 5,     /* O or LSE overlaps Q, K, V or each other        */
     FA_ERR_LAUNCH = 6,    /* the HIP launch reported an error               */
     FA_ERR_ALIGN = 7,     /* a pointer is not aligned to 16 bytes           */
-    FA_ERR_VARIANT = 8    /* fa_fwd_ex: Hq % Hkv != 0, S == 0, bad offset or window */
+    FA_ERR_VARIANT = 8    /* fa_fwd_ex/_split: Hq % Hkv, S == 0, offset, window, nsplit */
 };
 
 /*
@@ -147,6 +147,53 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 /* Host-side argument check of fa_fwd_ex without any HIP call. */
 int fa_check_args_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, int B, int Hq,
                      int Hkv, int T, int S, int d, float scale, int causal, int offset, int window);
+
+/*
+ * Split-KV form of fa_fwd_ex (flash-decoding): the keys are cut into G
+ * chunks, each (query tile, chunk) pair is its own work unit, and a second
+ * kernel merges the partial results.  For short query sequences (decode:
+ * T = 1) this gives the GPU B * Hq * G work units instead of B * Hq.
+ *
+ * What is computed, following "15. FlashAttention"
+ * (inference.shantanugoel.com), section "Decode is different:
+ * flash-decoding": chunk g holds keys [g * C, (g + 1) * C); for each query
+ * row it yields the softmax output O_g over that chunk's visible keys and
+ * their log-sum-exp L_g (O_g = 0, L_g = -inf where the row sees none of
+ * them); then L = log sum_g exp(L_g) and O = sum_g exp(L_g - L) O_g.  The
+ * result is the same attention as fa_fwd_ex (equal up to rounding order).
+ *
+ * Arguments:
+ *   q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window,
+ *          stream: as for fa_fwd_ex (o and lse receive the merged result).
+ *   nsplit requested number of chunks, 1 <= nsplit <= 4096.  The chunk
+ *          length is C = ceil(ceil(S / nsplit) / 128) * 128 keys (whole
+ *          key tiles) and the number of chunks used is G = ceil(S / C) =
+ *          fa_split_chunks(S, nsplit) <= nsplit.
+ *   ws_o   fp32 [G, B, Hq, T, d] workspace (device memory, 16-byte
+ *          aligned), owned by the caller; on return it holds the partials
+ *          O_g.
+ *   ws_lse fp32 [G, B, Hq, T] workspace (device memory), owned by the
+ *          caller; on return it holds L_g.
+ * When G == 1 the call is fa_fwd_ex itself and the workspaces are neither
+ * used nor checked (they may be NULL).
+ * Errors as for fa_fwd_ex, plus FA_ERR_VARIANT for nsplit outside
+ * [1, 4096], FA_ERR_NULL / FA_ERR_ALIGN for a missing or misaligned
+ * workspace and FA_ERR_ALIAS when a workspace overlaps an input, an output
+ * or the other workspace.  Two kernels run in order on `stream`; nothing
+ * is allocated and no atomics are used, so results are deterministic.
+ */
+int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int T,
+                 int S, int d, float scale, int causal, int offset, int window, int nsplit, float* ws_o,
+                 float* ws_lse, hipStream_t stream);
+
+/* Number of key chunks G that fa_fwd_split uses for S keys and a requested
+ * nsplit (1 for S <= 0 or nsplit < 1); sizes its workspaces. */
+int fa_split_chunks(int S, int nsplit);
+
+/* Host-side argument check of fa_fwd_split without any HIP call. */
+int fa_check_args_split(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+                        int Hq, int Hkv, int T, int S, int d, float scale, int causal, int offset, int window,
+                        int nsplit, const float* ws_o, const float* ws_lse);
 
 /*
  * Backward pass of fa_fwd (bf16): the gradients dQ, dK, dV of sum(O * dO)

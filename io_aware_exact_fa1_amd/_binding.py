@@ -1,9 +1,9 @@
 """ctypes binding of the C ABI in ``include/fa.h`` (argument marshalling only).
 
-The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_fwd_ex``, ``fa_bwd``,
-``fa_strerror``, ``fa_check_args``, ``fa_check_args_ex`` and
-``fa_bwd_check_args`` have the names and argument order of the C entry
-points; tensors are passed
+The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_fwd_ex``, ``fa_fwd_split``,
+``fa_bwd``, ``fa_strerror``, ``fa_check_args``, ``fa_check_args_ex``,
+``fa_check_args_split``, ``fa_split_chunks`` and ``fa_bwd_check_args`` have
+the names and argument order of the C entry points; tensors are passed
 as their device pointers and streams as HIP stream handles.  Every step of
 the computation runs in the HIP library: there is no fallback path, and a
 missing or unloadable library raises.
@@ -26,8 +26,8 @@ FA_ERR_LAUNCH = 6
 FA_ERR_ALIGN = 7
 FA_ERR_VARIANT = 8
 
-EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_bwd", "fa_strerror", "fa_check_args", "fa_check_args_ex",
-            "fa_bwd_check_args")
+EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_split", "fa_bwd", "fa_strerror", "fa_check_args",
+            "fa_check_args_ex", "fa_check_args_split", "fa_split_chunks", "fa_bwd_check_args")
 
 _lib = None
 
@@ -67,6 +67,12 @@ def load_library(path=None):
     lib.fa_fwd_ex.restype = i
     lib.fa_check_args_ex.argtypes = [vp] * 5 + [i, i, i, i, i, i, f, i, i, i]
     lib.fa_check_args_ex.restype = i
+    lib.fa_fwd_split.argtypes = [vp] * 5 + [i, i, i, i, i, i, f, i, i, i, i, vp, vp, vp]
+    lib.fa_fwd_split.restype = i
+    lib.fa_check_args_split.argtypes = [vp] * 5 + [i, i, i, i, i, i, f, i, i, i, i, vp, vp]
+    lib.fa_check_args_split.restype = i
+    lib.fa_split_chunks.argtypes = [i, i]
+    lib.fa_split_chunks.restype = i
     lib.fa_bwd.argtypes = [vp] * 10 + [i, i, i, i, f, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_check_args.argtypes = [vp] * 10 + [i, i, i, i, f, i]
@@ -110,6 +116,27 @@ def fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, windo
     return load_library().fa_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq), int(Hkv),
                                     int(T), int(S), int(d), float(scale), int(causal), int(offset), int(window),
                                     _stream(stream))
+
+
+def fa_fwd_split(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window, nsplit, ws_o, ws_lse,
+                 stream=None):
+    """C ``fa_fwd_split``: as ``fa_fwd_ex`` plus nsplit and the fp32
+    workspaces ws_o [G, B, Hq, T, d] and ws_lse [G, B, Hq, T]."""
+    return load_library().fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq), int(Hkv),
+                                       int(T), int(S), int(d), float(scale), int(causal), int(offset), int(window),
+                                       int(nsplit), _ptr(ws_o), _ptr(ws_lse), _stream(stream))
+
+
+def fa_check_args_split(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window, nsplit, ws_o,
+                        ws_lse):
+    return load_library().fa_check_args_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq),
+                                              int(Hkv), int(T), int(S), int(d), float(scale), int(causal),
+                                              int(offset), int(window), int(nsplit), _ptr(ws_o), _ptr(ws_lse))
+
+
+def fa_split_chunks(S, nsplit):
+    """Number of key chunks G that ``fa_fwd_split`` uses."""
+    return load_library().fa_split_chunks(int(S), int(nsplit))
 
 
 def fa_check_args_ex(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window):
@@ -238,3 +265,46 @@ def forward_ex(q, k, v, causal=False, scale=None, offset=None, window=0, stream=
         raise FaError(st, "fa_fwd_ex")
     return out, lse
 
+
+def forward_split(q, k, v, causal=False, scale=None, offset=None, window=0, nsplit=8, workspace=None,
+                  stream=None):
+    """``forward_ex`` through ``fa_fwd_split``: the keys are cut into
+    G = fa_split_chunks(S, nsplit) chunks whose partial results are merged.
+    ``workspace`` may be a (ws_o [G, B, Hq, T, d], ws_lse [G, B, Hq, T])
+    pair of float32 CUDA tensors to use (and read back afterwards); else
+    they are allocated here.  Returns (O, LSE)."""
+    import math
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, T, d] and k, v one [B, Hkv, S, d] shape")
+    if q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
+        raise ValueError("q, k and v must share B and d")
+    if any(x.dtype != torch.bfloat16 for x in (q, k, v)):
+        raise ValueError("fa_fwd_split takes bfloat16 tensors")
+    B, Hq, T, d = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    q, k, v = (x.contiguous() for x in (q, k, v))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if offset is None:
+        offset = S - T
+    G = fa_split_chunks(S, nsplit)
+    if workspace is None:
+        ws_o = torch.empty((G, B, Hq, T, d), dtype=torch.float32, device=q.device)
+        ws_lse = torch.empty((G, B, Hq, T), dtype=torch.float32, device=q.device)
+    else:
+        ws_o, ws_lse = workspace
+        if (ws_o.dtype != torch.float32 or ws_lse.dtype != torch.float32 or not ws_o.is_contiguous()
+                or not ws_lse.is_contiguous() or ws_o.numel() < G * B * Hq * T * d
+                or ws_lse.numel() < G * B * Hq * T):
+            raise ValueError("workspace must be contiguous float32 tensors of G*B*Hq*T*d and G*B*Hq*T elements")
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = fa_fwd_split(q, k, v, out, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window, nsplit, ws_o,
+                          ws_lse, stream)
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_split")
+    return out, lse

@@ -381,9 +381,16 @@ __device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
 // Arguments of the variants (EXT = true): query rows T and key rows S per
 // head, Hq query heads of which each group of `group` reads one K/V head,
 // the position of query row 0 (causal), a sliding window (0: none) and
-// whether work units pair a heavy and a light query tile.
+// whether work units pair a heavy and a light query tile.  Split-KV
+// (nsplit > 1): a work unit is (query tile, split); split g covers keys
+// [g * chunk, (g + 1) * chunk) and writes its normalised fp32 partial O_g
+// and LSE_g (-inf for a row with no visible key in the chunk) to
+// ws_o [nsplit, BH, T, d] and ws_lse [nsplit, BH, T] (BH = B * Hq).
 struct ExtArgs {
   int T, S, Hq, group, offset, window, pair;
+  int nsplit, chunk, BH;
+  float* ws_o;
+  float* ws_lse;
 };
 
 // EXACT = false: the fast kernel over every query tile.  EXACT = true: the
@@ -423,6 +430,12 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     tiles[0] = ur;
     tiles[1] = ur;
   }
+  const bool split_mode = EXT && ex.nsplit > 1;
+  int split = 0;
+  if (split_mode) {
+    split = ur % ex.nsplit;
+    tiles[0] = tiles[1] = ur / ex.nsplit;
+  }
 
   LaneOffsets<C> lo;
   lane_offsets<C>(lo, (unsigned)(uintptr_t)(const unsigned char LDS_AS*)smem, w, lane);
@@ -452,7 +465,8 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     if (EXACT) {
       const int query = qw0 + l32;
       if (query < Nq) {
-        const float x = lse[(size_t)bh * Nq + query];
+        const float x = split_mode ? ex.ws_lse[((size_t)split * ex.BH + bh) * Nq + query]
+                                   : lse[(size_t)bh * Nq + query];
         mine = x != x;
       }
       if (lane == 0) wave_marked[w] = __builtin_amdgcn_ballot_w64(mine) != 0;
@@ -478,9 +492,13 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       }
     }
 
-    const int kv_end = CAUSAL ? min(Nk, qoff + q0 + C::BR) : Nk;
+    int kv_end = CAUSAL ? min(Nk, qoff + q0 + C::BR) : Nk;
     // EXT with a window: the first key tile any query of the tile can see
-    const int kt0 = (EXT && wnd > 0) ? __builtin_amdgcn_readfirstlane(max(0, qoff + q0 - wnd + 1) / C::BC) : 0;
+    int kt0 = (EXT && wnd > 0) ? __builtin_amdgcn_readfirstlane(max(0, qoff + q0 - wnd + 1) / C::BC) : 0;
+    if (split_mode) {  // this unit's chunk of keys
+      kv_end = min(kv_end, (split + 1) * ex.chunk);
+      kt0 = max(kt0, split * (ex.chunk / C::BC));
+    }
     const int nkv = (kv_end + C::BC - 1) / C::BC - kt0;  // key tiles kt0 .. kt0 + nkv - 1
     // leading tiles that need no mask for any query of the workgroup
     int nfull = min(nkv, N / C::BC);
@@ -493,7 +511,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       // first visible key, so that every row has set its reference before
       const int glast = min(Nk / C::BC, CAUSAL ? (qoff + q0 + 1) / C::BC : Nk / C::BC);
       const int gfirst = wnd > 0 ? max(0, qoff + q0 + C::BR - wnd) / C::BC + 1 : 1;
-      nfull = max(0, glast - kt0);
+      nfull = max(0, min(nkv, glast - kt0));  // (split-KV: within the chunk)
       const int jh = max(1, gfirst - kt0);
       jhead = jh + ((1 - jh) & 3);  // the first j >= jh with j % 4 == 1 (unrolled stage order)
     }
@@ -506,6 +524,8 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
     bool jumped = false;
 
+    // (split-KV: a chunk beyond every row's last visible key has no tiles)
+    if (!EXT || nkv > 0) {
     // Phases.  Each step j of a wave is a matrix-core phase M(j) -- S_j =
     // K_j Q^T and acc += V_{j-1}^T P_{j-1}^T -- followed by a vector-ALU
     // phase V(j) -- the softmax of S_j into P_j -- with a workgroup barrier
@@ -740,13 +760,33 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       barrier();  // every wave is done with the LDS ring before it is refilled
     }
 
+    }
+
     // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
     const float lt = half_sum(lsum);
     // a row is marked when either half of its keys flagged a jump
     jumped = half_max(jumped ? 1.f : 0.f) != 0.f;
-    const float inv = 1.f / lt;
+    // (split-KV: no visible key in this chunk -> O_g = 0, LSE_g = -inf)
+    const bool empty = EXT && !(lt > 0.f);
+    const float inv = empty ? 0.f : 1.f / lt;
     const int query = qw0 + l32;
-    if (query < Nq && (!EXACT || mine)) {  // the recompute kernel stores only marked rows
+    if (split_mode && query < Nq && (!EXACT || mine)) {
+      const size_t prow = ((size_t)split * ex.BH + bh) * Nq + query;
+      float* orow = ex.ws_o + prow * C::D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float4 ov;
+          ov.x = acc[db][4 * a + 0] * inv;
+          ov.y = acc[db][4 * a + 1] * inv;
+          ov.z = acc[db][4 * a + 2] * inv;
+          ov.w = acc[db][4 * a + 3] * inv;
+          *(float4*)(orow + 32 * db + 8 * a + 4 * h) = ov;
+        }
+      if (h == 0)
+        ex.ws_lse[prow] = jumped ? __builtin_nanf("") : (empty ? -INFINITY : (m + __log2f(lt)) * kLn2);
+    } else if (query < Nq && (!EXACT || mine)) {  // the recompute kernel stores only marked rows
       uint16_t* orow = o + hoff + (size_t)query * C::D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -885,15 +925,16 @@ void launch_bf16(const void* q, const void* k, const void* v, void* o, float* ls
 
 template <class C, bool CAUSAL>
 void launch_bf16_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-                    int T, int S, int offset, int window, float c, unsigned qsign, hipStream_t stream) {
+                    int T, int S, int offset, int window, float c, unsigned qsign, hipStream_t stream,
+                    int nsplit = 1, int chunk = 0, float* ws_o = nullptr, float* ws_lse = nullptr) {
   const int T_r = (T + C::BR - 1) / C::BR;
-  // with a window every query tile costs about the same: no pairing
-  const int pair = CAUSAL && window == 0;
-  const int units_per_head = pair ? (T_r + 1) / 2 : T_r;
+  // with a window (or split keys) every unit costs about the same: no pairing
+  const int pair = CAUSAL && window == 0 && nsplit == 1;
+  const int units_per_head = pair ? (T_r + 1) / 2 : T_r * nsplit;
   const int num_units = B * Hq * units_per_head;
   const int per_xcd = (num_units + 7) / 8;
   const int grid = per_xcd * 8;
-  const ExtArgs ex{T, S, Hq, Hq / Hkv, offset, window, pair};
+  const ExtArgs ex{T, S, Hq, Hq / Hkv, offset, window, pair, nsplit, chunk, B * Hq, ws_o, ws_lse};
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, false, true>), dim3(grid), dim3(C::NW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, T, T_r,
                      units_per_head, num_units, per_xcd, c, qsign, ex);
@@ -926,6 +967,44 @@ int check_ex(const void* q, const void* k, const void* v, const void* o, const f
       overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, kb) || overlaps(lse, lb, o, qb))
     return FA_ERR_ALIAS;
   return FA_OK;
+}
+
+// Split-KV merge ("15. FlashAttention", section "Decode is different:
+// flash-decoding"): per row, L = log sum_g exp(L_g) and
+// O = sum_g exp(L_g - L) O_g over the nsplit partials (a partial with
+// L_g = -inf, a chunk the row sees no key of, has weight 0).  D/4 lanes
+// per row, four dims per lane: 8 rows (d = 128) or 16 rows (d = 64) per
+// 256-thread workgroup.  The partials are read once, coalesced.
+template <int D>
+__global__ void __launch_bounds__(256)
+fa_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, uint16_t* __restrict__ o,
+                float* __restrict__ lse, long long rows, int nsplit) {
+  constexpr int LPR = D / 4;  // lanes per row
+  const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int g = 0; g < nsplit; ++g) mx = fmaxf(mx, ws_lse[(long long)g * rows + row]);
+  float tot = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int g = 0; g < nsplit; ++g) {
+    const float lg = ws_lse[(long long)g * rows + row];
+    if (lg == -INFINITY) continue;
+    const float wgt = __expf(lg - mx);
+    const float4 x = *(const float4*)(ws_o + ((long long)g * rows + row) * D + 4 * part);
+    tot += wgt;
+    a0 = fmaf(wgt, x.x, a0);
+    a1 = fmaf(wgt, x.y, a1);
+    a2 = fmaf(wgt, x.z, a2);
+    a3 = fmaf(wgt, x.w, a3);
+  }
+  const float inv = 1.f / tot;
+  bf16x4 ov;
+  ov[0] = (__bf16)(a0 * inv);
+  ov[1] = (__bf16)(a1 * inv);
+  ov[2] = (__bf16)(a2 * inv);
+  ov[3] = (__bf16)(a3 * inv);
+  *(u32x2*)(o + row * D + 4 * part) = __builtin_bit_cast(u32x2, ov);
+  if (part == 0) lse[row] = mx + __logf(tot);
 }
 
 template <int D, bool CAUSAL>
@@ -1013,6 +1092,76 @@ extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, f
   } else {
     if (causal) launch_bf16_ex<CfgD64, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream);
     else launch_bf16_ex<CfgD64, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream);
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// Key chunk of each split: whole 128-key tiles (a multiple of both key tile
+// widths), so that no tile straddles two chunks.
+static int split_chunk(int S, int nsplit) { return ((S + nsplit - 1) / nsplit + 127) / 128 * 128; }
+
+extern "C" int fa_split_chunks(int S, int nsplit) {
+  if (S <= 0 || nsplit < 1) return 1;
+  const int chunk = split_chunk(S, nsplit);
+  return (S + chunk - 1) / chunk;
+}
+
+extern "C" int fa_check_args_split(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                   int B, int Hq, int Hkv, int T, int S, int d, float scale, int causal,
+                                   int offset, int window, int nsplit, const float* ws_o, const float* ws_lse) {
+  const int st = check_ex(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window);
+  if (st != FA_OK) return st;
+  if (nsplit < 1 || nsplit > 4096) return FA_ERR_VARIANT;
+  const long long rows = (long long)B * Hq * T;
+  if (rows == 0 || fa_split_chunks(S, nsplit) == 1) return FA_OK;  // no workspace used
+  const int g = fa_split_chunks(S, nsplit);
+  if (!ws_o || !ws_lse) return FA_ERR_NULL;
+  if (((uintptr_t)ws_o & 15) || ((uintptr_t)ws_lse & 3)) return FA_ERR_ALIGN;
+  if ((long long)B * Hq * ((T + 31) / 32) * g > (1LL << 30)) return FA_ERR_SHAPE;
+  const size_t wob = (size_t)g * rows * d * 4, wlb = (size_t)g * rows * 4;
+  const size_t qb = (size_t)rows * d * 2, kb = (size_t)B * Hkv * S * d * 2, lb = (size_t)rows * 4;
+  const void* all[5] = {q, k, v, o, lse};
+  const size_t sz[5] = {qb, kb, kb, qb, lb};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(ws_o, wob, all[i], sz[i]) || overlaps(ws_lse, wlb, all[i], sz[i])) return FA_ERR_ALIAS;
+  if (overlaps(ws_o, wob, ws_lse, wlb)) return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+extern "C" int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                            int Hkv, int T, int S, int d, float scale, int causal, int offset, int window,
+                            int nsplit, float* ws_o, float* ws_lse, hipStream_t stream) {
+  const int st = fa_check_args_split(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window, nsplit,
+                                     ws_o, ws_lse);
+  if (st != FA_OK) return st;
+  const long long rows = (long long)B * Hq * T;
+  if (rows == 0) return FA_OK;
+  const int g = fa_split_chunks(S, nsplit);
+  if (g == 1)  // one chunk: the direct path
+    return fa_fwd_ex(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window, stream);
+  const int chunk = split_chunk(S, nsplit);
+  const unsigned qsign = (scale < 0.f) ? 0x80008000u : 0u;  // as in fa_fwd
+  const float c = scale == 0.f ? 0x1p-100f : fabsf(scale) * kLog2e;
+  const int off = causal ? offset : 0;
+  const int wnd = causal ? window : 0;
+  if (d == 128) {
+    if (causal)
+      launch_bf16_ex<CfgD128, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream, g, chunk, ws_o,
+                                    ws_lse);
+    else
+      launch_bf16_ex<CfgD128, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream, g, chunk, ws_o,
+                                     ws_lse);
+    hipLaunchKernelGGL(fa_merge_kernel<128>, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream, ws_o, ws_lse,
+                       (uint16_t*)o, lse, rows, g);
+  } else {
+    if (causal)
+      launch_bf16_ex<CfgD64, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream, g, chunk, ws_o,
+                                   ws_lse);
+    else
+      launch_bf16_ex<CfgD64, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream, g, chunk, ws_o,
+                                    ws_lse);
+    hipLaunchKernelGGL(fa_merge_kernel<64>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, ws_o, ws_lse,
+                       (uint16_t*)o, lse, rows, g);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

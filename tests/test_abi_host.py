@@ -25,7 +25,12 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(["fa_bwd", "fa_bwd_check_args", "fa_check_args", "fa_check_args_ex",
-                                           "fa_fwd", "fa_fwd_ex", "fa_fwd_f32", "fa_strerror"])
+                                           "fa_check_args_split", "fa_fwd", "fa_fwd_ex", "fa_fwd_f32",
+                                           "fa_fwd_split", "fa_split_chunks", "fa_strerror"])
+
+
+def test_binding_exports_match_the_header():
+    assert sorted(fa.EXPORTED) == declared_functions()
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -176,3 +181,60 @@ def test_ex_check_args_ok():
 def test_ex_check_args_errors(kw, code):
     assert _ex(**kw) == code
 
+
+WO, WL = 0x60000000, 0x70000000
+
+
+def _split(**kw):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, Hq=8, Hkv=2, T=1, S=4000, d=128, scale=0.1, causal=1, offset=3999,
+             window=0, nsplit=8, ws_o=WO, ws_lse=WL)
+    a.update(kw)
+    return fa.fa_check_args_split(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["T"],
+                                  a["S"], a["d"], a["scale"], a["causal"], a["offset"], a["window"], a["nsplit"],
+                                  a["ws_o"], a["ws_lse"])
+
+
+@pytest.mark.parametrize("S,nsplit,G", [
+    (1, 1, 1), (1, 8, 1), (128, 2, 1), (129, 2, 2), (300, 4, 3), (4000, 8, 8), (16384, 8, 8), (16384, 3, 3),
+    (16384, 4096, 128), (1000, 1000, 8), (0, 4, 1), (100, 0, 1),
+])
+def test_split_chunks(S, nsplit, G):
+    """G = ceil(S / C) with C = ceil(ceil(S / nsplit) / 128) * 128: whole
+    128-key chunks, never more than nsplit of them."""
+    assert fa.fa_split_chunks(S, nsplit) == G
+    if S > 0 and nsplit > 0:
+        C = -(-(-(-S // nsplit)) // 128) * 128
+        assert G == -(-S // C) and G <= nsplit and (G - 1) * C < S <= G * C
+
+
+def test_split_check_args_ok():
+    assert _split() == fa.FA_OK
+    assert _split(nsplit=1, ws_o=None, ws_lse=None) == fa.FA_OK     # one chunk: no workspace
+    assert _split(S=100, offset=99, ws_o=None, ws_lse=None) == fa.FA_OK
+    assert _split(T=100, offset=0, window=300) == fa.FA_OK
+    assert _split(causal=0, T=7) == fa.FA_OK
+    assert _split(B=0, q=None, ws_o=None) == fa.FA_OK                  # empty
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nsplit=0), fa.FA_ERR_VARIANT),
+    (dict(nsplit=4097), fa.FA_ERR_VARIANT),
+    (dict(ws_o=None), fa.FA_ERR_NULL),
+    (dict(ws_lse=None), fa.FA_ERR_NULL),
+    (dict(ws_o=WO + 8), fa.FA_ERR_ALIGN),
+    (dict(ws_lse=WL + 2), fa.FA_ERR_ALIGN),
+    (dict(ws_o=K), fa.FA_ERR_ALIAS),
+    (dict(ws_lse=O), fa.FA_ERR_ALIAS),
+    (dict(ws_lse=WO + 64), fa.FA_ERR_ALIAS),
+    (dict(Hkv=3), fa.FA_ERR_VARIANT),             # the fa_fwd_ex checks come first
+    (dict(d=80), fa.FA_ERR_HEAD_DIM),
+])
+def test_split_check_args_errors(kw, code):
+    assert _split(**kw) == code
+
+
+def test_split_rejects_on_the_host():
+    assert fa.fa_fwd_split(Q, K, V, O, L, 1, 2, 2, 1, 1000, 128, 0.1, 1, 999, 0, 0, WO, WL, 0) == fa.FA_ERR_VARIANT
+    assert fa.fa_fwd_split(Q, K, V, O, L, 1, 2, 2, 1, 1000, 128, 0.1, 1, 999, 0, 4, None, WL, 0) == fa.FA_ERR_NULL
+    assert fa.fa_fwd_split(None, None, None, None, None, 0, 2, 2, 1, 1000, 128, 0.1, 1, 999, 0, 4, None, None,
+                           0) == fa.FA_OK
