@@ -33,7 +33,10 @@ heads, a sliding window (0: none) and T query rows at the newest positions
 of the N keys (default T = N); FLOPs then count the visible (query, key)
 pairs.  nsplit > 1 runs fa_fwd_split (split-KV with that many key chunks,
 then the merge) instead; kv_gbs is then the K/V bytes read once per step
-over the step time, the bound of decode (T = 1).
+over the step time, the bound of decode (T = 1).  With --graph the timed
+calls are captured once in a HIP graph and replayed, so that the time is the
+GPU's and not the host's launch overhead (which dominates calls of a few
+tens of microseconds); the graph's output is checked against the eager one.
 """
 
 import argparse
@@ -70,6 +73,8 @@ def parse():
                    help="time the backward pass (fa_bwd) instead of the forward")
     p.add_argument("--shapes", default=None,
                    help="semicolon-separated B,H,N,d,causal shapes to run one after the other (forward, bf16)")
+    p.add_argument("--graph", action="store_true",
+                   help="--shapes: capture the timed calls in one HIP graph (no host launch overhead)")
     p.add_argument("--copy-cal", action="store_true",
                    help="run only a plain device copy of 1 GiB (5 times), to calibrate the HBM "
                         "byte counters (FETCH_SIZE / WRITE_SIZE) of a profiler run")
@@ -226,24 +231,39 @@ def shape_sweep(args):
         entry = "fa_fwd_split" if nsplit > 1 else ("fa_fwd_ex" if ext else "fa_fwd")
 
         def step():
+            cs = torch.cuda.current_stream().cuda_stream  # (the capture stream under --graph)
             if nsplit > 1:
                 st = fa.fa_fwd_split(qd, kd, vd, o, lse, B, H, hkv, T, N, d, scale, causal, N - T, window, nsplit,
-                                     ws_o, ws_l, stream.cuda_stream)
+                                     ws_o, ws_l, cs)
             elif ext:
-                st = fa.fa_fwd_ex(qd, kd, vd, o, lse, B, H, hkv, T, N, d, scale, causal, N - T, window,
-                                  stream.cuda_stream)
+                st = fa.fa_fwd_ex(qd, kd, vd, o, lse, B, H, hkv, T, N, d, scale, causal, N - T, window, cs)
             else:
-                st = fa.fa_fwd(qd, kd, vd, o, lse, B, H, N, d, scale, causal, stream.cuda_stream)
+                st = fa.fa_fwd(qd, kd, vd, o, lse, B, H, N, d, scale, causal, cs)
             if st != fa.FA_OK:
                 raise fa.FaError(st, entry)
 
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
+        graph_ok = None
+        if args.graph:
+            ref_o, ref_l = o.clone(), lse.clone()
+            o.zero_()
+            lse.zero_()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(args.steps):
+                    step()
+            graph.replay()  # warm replay
+            torch.cuda.synchronize()
+            graph_ok = bool(torch.equal(o, ref_o) and torch.equal(lse, ref_l))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(args.steps):
-            step()
+        if args.graph:
+            graph.replay()
+        else:
+            for _ in range(args.steps):
+                step()
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
@@ -262,7 +282,10 @@ def shape_sweep(args):
                           "kv_gbs": round(2.0 * B * hkv * N * d * 2 / ms / 1e6, 1),
                           "once_bytes": workloads.hbm_once_bytes(B, H, N, d),
                           "stream_bytes": workloads.tile_stream_bytes(B, H, N, d, br, bc, bool(causal)),
-                          "tile": {"Br": br, "Bc": bc}}), flush=True)
+                          "tile": {"Br": br, "Bc": bc}, "graph": args.graph, "graph_equals_eager": graph_ok}),
+              flush=True)
+        if args.graph:
+            del graph
         del qd, kd, vd, o, lse, ws_o, ws_l
 
 

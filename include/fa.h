@@ -174,13 +174,23 @@ int fa_check_args_ex(const void* q, const void* k, const void* v, const void* o,
  *          O_g.
  *   ws_lse fp32 [G, B, Hq, T] workspace (device memory), owned by the
  *          caller; on return it holds L_g.
- * When G == 1 the call is fa_fwd_ex itself and the workspaces are neither
- * used nor checked (they may be NULL).
+ * Two kernels serve this.  With at most 32 query rows per K/V head
+ * ((Hq / Hkv) * T <= 32: decode, short chunked prefill) a small-tile kernel
+ * runs one workgroup per (batch, K/V head, chunk), the query heads of the
+ * group times the T rows forming the 32 columns of its matrix products, so
+ * that each K/V byte is read once; with one chunk it writes O and LSE
+ * itself.  Otherwise each (256-row query tile, chunk) is a work unit of
+ * the fa_fwd_ex kernel, and with one chunk the call is fa_fwd_ex itself.
+ * When G == 1 the workspaces are neither used nor checked (they may be
+ * NULL).
  * Errors as for fa_fwd_ex, plus FA_ERR_VARIANT for nsplit outside
  * [1, 4096], FA_ERR_NULL / FA_ERR_ALIGN for a missing or misaligned
- * workspace and FA_ERR_ALIAS when a workspace overlaps an input, an output
- * or the other workspace.  Two kernels run in order on `stream`; nothing
- * is allocated and no atomics are used, so results are deterministic.
+ * workspace, FA_ERR_ALIAS when a workspace overlaps an input, an output
+ * or the other workspace, and FA_ERR_SHAPE when a launch would exceed
+ * 2^32 work items.  The kernels run in order on `stream` (the partial
+ * kernel, then for G > 1 the merge); nothing is allocated, no memset is
+ * issued and no atomics are used, so results are deterministic and the
+ * call can be captured in a HIP graph.
  */
 int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int T,
                  int S, int d, float scale, int causal, int offset, int window, int nsplit, float* ws_o,

@@ -238,3 +238,15 @@ def test_split_rejects_on_the_host():
     assert fa.fa_fwd_split(Q, K, V, O, L, 1, 2, 2, 1, 1000, 128, 0.1, 1, 999, 0, 4, None, WL, 0) == fa.FA_ERR_NULL
     assert fa.fa_fwd_split(None, None, None, None, None, 0, 2, 2, 1, 1000, 128, 0.1, 1, 999, 0, 4, None, None,
                            0) == fa.FA_OK
+
+
+def test_split_rejects_launches_past_32_bit_work_items():
+    """4096 x 64 K/V heads in 64 chunks: 2^24 small-tile workgroups of 256
+    work items do not fit one dispatch."""
+    P = [(i + 1) << 44 for i in range(7)]
+    st = fa.fa_check_args_split(P[0], P[1], P[2], P[3], P[4], 4096, 64, 64, 1, 8192, 128, 0.1, 1, 8191, 0, 64,
+                                P[5], P[6])
+    assert st == fa.FA_ERR_SHAPE
+    st = fa.fa_check_args_split(P[0], P[1], P[2], P[3], P[4], 4096, 64, 64, 1, 8192, 128, 0.1, 1, 8191, 0, 32,
+                                P[5], P[6])
+    assert st == fa.FA_OK

@@ -112,9 +112,10 @@ def test_cross_attention(T, S):
 
 
 def test_single_chunk_is_fa_fwd_ex_bitwise():
-    """G = 1 (nsplit 1, or S <= 128): the direct path, workspace unused."""
+    """G = 1 (nsplit 1) with more than 32 query rows per K/V head: the call
+    is fa_fwd_ex itself, workspace unused."""
     require_gpu()
-    q, k, v = _qkv(1, 4, 2, 5, 700, 128, seed=1)
+    q, k, v = _qkv(1, 4, 2, 17, 700, 128, seed=1)
     say("single chunk")
     o1, l1 = fa.forward_ex(q.cuda(), k.cuda(), v.cuda(), causal=True)
     o2, l2 = fa.forward_split(q.cuda(), k.cuda(), v.cuda(), causal=True, nsplit=1)
@@ -151,6 +152,31 @@ def test_deterministic_and_workspace_reuse():
     torch.cuda.synchronize()
     ro, rl = attention_ex_ref(f64(q2), f64(k2), f64(v2), 1 / np.sqrt(128), True)
     assert_close(f64(o), f64(lse), ro, rl, torch.bfloat16, "reuse")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("Hq,Hkv,T", [(1, 1, 32), (4, 1, 8), (8, 1, 3), (2, 2, 5), (16, 2, 2), (32, 4, 1)])
+def test_small_tile_rows(Hq, Hkv, T, d):
+    """Up to 32 query rows per K/V head (group * T <= 32): the small-tile
+    kernel, whose 32 columns hold the group's heads times the T rows;
+    causal with the newest positions, with an offset and a window, and
+    non-causal; one chunk (O and LSE written directly) and several."""
+    require_gpu()
+    S = 1000
+    q, k, v = _qkv(2, Hq, Hkv, T, S, d, seed=Hq * 100 + T + d)
+    for causal, off, w, ns in ((True, None, 0, 1), (True, None, 0, 4), (True, 500, 0, 3), (True, 700, 77, 5),
+                               (True, None, 300, 8), (False, None, 0, 1), (False, None, 0, 6)):
+        _check(q, k, v, causal, off, w, ns, f"small Hq={Hq} Hkv={Hkv} T={T} d={d} causal={causal} "
+               f"offset={off} window={w} nsplit={ns}")
+
+
+@pytest.mark.parametrize("S", [1, 31, 32, 33, 95, 128, 129, 4097])
+def test_small_tile_tails(S):
+    """Ragged key counts around the 32-key tiles and 128-key chunks."""
+    require_gpu()
+    q, k, v = _qkv(1, 8, 2, min(2, S), S, 128, seed=S)
+    for ns in (1, 2, 7):
+        _check(q, k, v, True, None, 0, ns, f"tails S={S} nsplit={ns}")
 
 
 @pytest.mark.parametrize("nsplit", [8, 16, 64])
