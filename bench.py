@@ -20,6 +20,12 @@ the forward's O and LSE) on the same workload instead; FLOPs are counted as
 2.5 times the forward's (the five N x N x d products of the backward, the
 recomputation of S included).
 
+With --configs, every workload of the five configs is timed in turn (one
+JSON line each): HIP-graph replay of the timed calls (GPU time) and eager
+calls, TFLOP/s against the bf16 matrix peak (fp32 vector peak for the fp32
+config) and algorithmic GB/s against HBM; the small configs also run
+through fa_fwd_split.
+
 With --shapes "B,H,N,d,causal;...", each listed shape (bf16, seeded N(0,1)
 inputs) is run in turn and one JSON line per shape is printed with its time
 and the two byte models of the pages (read-once bytes and tile-stream
@@ -73,6 +79,8 @@ def parse():
                    help="time the backward pass (fa_bwd) instead of the forward")
     p.add_argument("--shapes", default=None,
                    help="semicolon-separated B,H,N,d,causal shapes to run one after the other (forward, bf16)")
+    p.add_argument("--configs", action="store_true",
+                   help="time every workload of the five configs (one JSON line each), graph-replayed and eager")
     p.add_argument("--graph", action="store_true",
                    help="--shapes: capture the timed calls in one HIP graph (no host launch overhead)")
     p.add_argument("--copy-cal", action="store_true",
@@ -289,6 +297,82 @@ def shape_sweep(args):
         del qd, kd, vd, o, lse, ws_o, ws_l
 
 
+PEAK_FP32_TFLOPS = 157.3   # MI355X published fp32 vector peak (the fp32 config computes on the vector ALUs)
+PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
+
+
+def config_sweep(args):
+    """One JSON line per workload: fa_fwd (fa_fwd_f32 for fp32) time from a
+    HIP graph of `steps` calls and from eager calls, TFLOP/s against the
+    matrix (or, for fp32, vector) peak and algorithmic GB/s (Q, K, V read
+    once, O and LSE written once) against HBM; for the small configs also
+    fa_fwd_split, whose key chunks multiply the work units."""
+    import torch
+    import io_aware_exact_fa1_amd as fa
+    import workloads
+
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    for name, w in workloads.WORKLOADS.items():
+        q, k, v = (x.to(dev) for x in workloads.make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, w.k_mult))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        variants = [("fa_fwd_f32" if w.dtype == "f32" else "fa_fwd", 1)]
+        if w.dtype == "bf16" and w.B * w.H * -(-w.N // 256) < 512:
+            variants += [("fa_fwd_split", n) for n in (2, 4)]
+        for entry, nsplit in variants:
+            G = fa.fa_split_chunks(w.N, nsplit)
+            ws = (torch.empty((G, w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev),
+                  torch.empty((G, w.B, w.H, w.N), dtype=torch.float32, device=dev)) if nsplit > 1 else (None, None)
+
+            def step():
+                cs = torch.cuda.current_stream().cuda_stream
+                if entry == "fa_fwd_f32":
+                    st = fa.fa_fwd_f32(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, cs)
+                elif entry == "fa_fwd":
+                    st = fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, w.scale, w.causal, cs)
+                else:
+                    st = fa.fa_fwd_split(q, k, v, o, lse, w.B, w.H, w.H, w.N, w.N, w.d, w.scale, w.causal, 0, 0,
+                                         nsplit, ws[0], ws[1], cs)
+                if st != fa.FA_OK:
+                    raise fa.FaError(st, entry)
+
+            for _ in range(args.warmup):
+                step()
+            torch.cuda.synchronize()
+            ref_o, ref_l = o.clone(), lse.clone()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(args.steps):
+                    step()
+            graph.replay()
+            torch.cuda.synchronize()
+            same = bool(torch.equal(o, ref_o) and torch.equal(lse, ref_l))
+            stream = torch.cuda.current_stream()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            e0.record(stream)
+            for _ in range(args.steps):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_eager = e0.elapsed_time(e1) / args.steps
+            peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+            tf = w.flops / ms / 1e9
+            gbs = w.algorithmic_bytes / ms / 1e6
+            print(json.dumps({"workload": name, "note": w.note, "entry": entry, "nsplit": nsplit, "chunks": G,
+                              "ms": round(ms, 5), "ms_eager": round(ms_eager, 5),
+                              "tflops": round(tf, 2), "peak_tflops": peak, "frac_peak": round(tf / peak, 4),
+                              "algorithmic_bytes": w.algorithmic_bytes, "gbs": round(gbs, 1),
+                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "graph_equals_eager": same}), flush=True)
+            del graph, ws
+        del q, k, v, o, lse
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -299,6 +383,9 @@ def main():
 
     if args.copy_cal:
         copy_calibration()
+        return
+    if args.configs:
+        config_sweep(args)
         return
     if args.shapes:
         shape_sweep(args)

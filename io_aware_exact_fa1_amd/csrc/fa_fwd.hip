@@ -805,21 +805,29 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path: true fp32 arithmetic on the vector ALUs, one thread per query.
-constexpr int F32_BQ = 64;  // queries per workgroup (one wave)
+// fp32 path: true fp32 arithmetic on the vector ALUs.  A wave takes
+// 64 / KL queries; the KL lanes of a query take every KL-th key of each
+// LDS tile (lane kl: keys k0 + kl, k0 + kl + KL, ...) with their own online
+// softmax state (m, l, acc), merged across the KL lanes at the end (the
+// same log-sum-exp rule as a split over keys).  KL = 1 gives one query per
+// thread (large problems, where K/V tiles are shared by 64 queries); KL = 16
+// spreads small problems over 16 times more waves.
 constexpr int F32_BK = 32;  // keys per LDS tile
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int KL>
 __global__ void __launch_bounds__(64)
 fa_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
                   float* __restrict__ o, float* __restrict__ lse, int N, float c) {
+  constexpr int QW = 64 / KL;  // queries per wave
   __shared__ float ks[F32_BK][D];
   __shared__ float vs[F32_BK][D];
   const int t = threadIdx.x;
-  const int q0 = blockIdx.x * F32_BQ;
+  const int qi = t / KL, kl = t % KL;
+  const int q0 = blockIdx.x * QW;
   const int bh = blockIdx.y;
   const size_t hoff = (size_t)bh * (size_t)N * D;
-  const int query = q0 + t;
+  const int query = q0 + qi;
   const int qrow = min(query, N - 1);
 
   float qv[D];
@@ -830,27 +838,42 @@ fa_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k, cons
   for (int e = 0; e < D; ++e) acc[e] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  const int kv_end = CAUSAL ? min(N, q0 + F32_BQ) : N;
+  const int kv_end = CAUSAL ? min(N, q0 + QW) : N;
   for (int k0 = 0; k0 < kv_end; k0 += F32_BK) {
-    __syncthreads();
-    for (int idx = t; idx < F32_BK * D; idx += 64) {
-      const int r = idx / D, e = idx % D;
-      const int grow = min(k0 + r, N - 1);
-      ks[r][e] = k[hoff + (size_t)grow * D + e];
-      vs[r][e] = v[hoff + (size_t)grow * D + e];
+    // the tile's K and V rows as float4, every load of the tile issued
+    // before the first is used
+    constexpr int NL = F32_BK * D / 4 / 64;  // float4 per thread per matrix
+    f32x4v kx[NL], vx[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int idx = t + 64 * i;
+      const int r = idx / (D / 4), e4 = idx % (D / 4);
+      const size_t src = hoff + (size_t)min(k0 + r, N - 1) * D + 4 * e4;
+      kx[i] = *(const f32x4v*)(k + src);
+      vx[i] = *(const f32x4v*)(v + src);
     }
     __syncthreads();
-    float s[F32_BK];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int idx = t + 64 * i;
+      const int r = idx / (D / 4), e4 = idx % (D / 4);
+      *(f32x4v*)&ks[r][4 * e4] = kx[i];
+      *(f32x4v*)&vs[r][4 * e4] = vx[i];
+    }
+    __syncthreads();
+    constexpr int NJ = F32_BK / KL;  // keys of this tile per lane
+    float s[NJ];
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < F32_BK; ++j) {
+    for (int jj = 0; jj < NJ; ++jj) {
+      const int j = kl + KL * jj;
       float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < D; ++e) dot = fmaf(qv[e], ks[j][e], dot);
       const int key = k0 + j;
       const bool vis = key < N && (!CAUSAL || key <= query);
-      s[j] = vis ? dot * c : -INFINITY;
-      mx = fmaxf(mx, s[j]);
+      s[jj] = vis ? dot * c : -INFINITY;
+      mx = fmaxf(mx, s[jj]);
     }
     const float m_new = fmaxf(m, mx);
     const float mref = (m_new == -INFINITY) ? 0.f : m_new;
@@ -859,15 +882,34 @@ fa_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k, cons
 #pragma unroll
     for (int e = 0; e < D; ++e) acc[e] *= alpha;
 #pragma unroll
-    for (int j = 0; j < F32_BK; ++j) {
-      const float p = (s[j] == -INFINITY) ? 0.f : exp2f(s[j] - mref);
+    for (int jj = 0; jj < NJ; ++jj) {
+      const float p = (s[jj] == -INFINITY) ? 0.f : exp2f(s[jj] - mref);
       l += p;
 #pragma unroll
-      for (int e = 0; e < D; ++e) acc[e] = fmaf(p, vs[j][e], acc[e]);
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(p, vs[kl + KL * jj][e], acc[e]);
     }
     m = m_new;
   }
-  if (query < N) {
+  // merge the KL lanes of each query (lanes kl = 0 .. KL-1 are adjacent)
+  if (KL > 1) {
+    float mq = m;
+#pragma unroll
+    for (int off = 1; off < KL; off *= 2) mq = fmaxf(mq, __shfl_xor(mq, off, 64));
+    const float mref = (mq == -INFINITY) ? 0.f : mq;
+    const float sc = exp2f(m - mref);  // 0 for a lane that saw no key
+    l *= sc;
+#pragma unroll
+    for (int off = 1; off < KL; off *= 2) l += __shfl_xor(l, off, 64);
+#pragma unroll
+    for (int e = 0; e < D; ++e) {
+      float x = acc[e] * sc;
+#pragma unroll
+      for (int off = 1; off < KL; off *= 2) x += __shfl_xor(x, off, 64);
+      acc[e] = x;
+    }
+    m = mq;
+  }
+  if (query < N && kl == 0) {
     const float inv = 1.f / l;
 #pragma unroll
     for (int e = 0; e < D; ++e) o[hoff + (size_t)query * D + e] = acc[e] * inv;
@@ -972,65 +1014,80 @@ int check_ex(const void* q, const void* k, const void* v, const void* o, const f
 // Split-KV merge ("15. FlashAttention", section "Decode is different:
 // flash-decoding"): per row, L = log sum_g exp(L_g) and
 // O = sum_g exp(L_g - L) O_g over the G partials (a partial with
-// L_g = -inf, a chunk the row sees no key of, has weight 0).  One
-// workgroup per row: thread (gi, col) takes four output dims (col) of the
-// partials g = gi, gi + NGL, ..., so that the G partial rows are read in
-// parallel (coalesced float4) rather than one after another; the NGL
-// partial sums are then added in LDS.
-inline dim3 merge_grid(long long rows) {
-  return dim3((unsigned)(rows < 65536 ? rows : 65536), (unsigned)((rows + 65535) / 65536));
+// L_g = -inf, a chunk the row sees no key of, has weight 0).  A workgroup
+// of 256 threads takes RB rows; within a row, thread (gi, col) takes four
+// output dims (col) of the partials g = gi, gi + NGL, ..., so that the
+// partial rows are read in parallel (coalesced float4) rather than one
+// after another, and the NGL partial sums are added in LDS.  NGL is the
+// largest power of two <= min(G, 256 / (D/4)) and RB = 256 / (D/4) / NGL.
+inline int merge_ngl(int D, int G) {
+  int n = 1;
+  while (2 * n <= G && 2 * n <= 256 / (D / 4)) n *= 2;
+  return n;
+}
+
+inline dim3 merge_grid(long long rows, int D, int G) {
+  const long long rb = 256 / (D / 4) / merge_ngl(D, G);
+  const long long blocks = (rows + rb - 1) / rb;
+  return dim3((unsigned)(blocks < 65536 ? blocks : 65536), (unsigned)((blocks + 65535) / 65536));
 }
 
 template <int D>
 __global__ void __launch_bounds__(256)
 fa_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, uint16_t* __restrict__ o,
-                float* __restrict__ lse, long long rows, int nsplit) {
-  constexpr int NC = D / 4;     // float4 columns per row
-  constexpr int NGL = 256 / NC; // partials taken in parallel
-  __shared__ float smax[NGL];
-  __shared__ float stot[NGL];
-  __shared__ __attribute__((aligned(16))) float sacc[NGL][D];
-  // (a 2-D grid: 65536 rows per grid row)
-  const long long row = (long long)blockIdx.y * 65536 + blockIdx.x;
-  if (row >= rows) return;
-  const int col = threadIdx.x % NC, gi = threadIdx.x / NC;
+                float* __restrict__ lse, long long rows, int nsplit, int ngl) {
+  constexpr int NC = D / 4;       // float4 columns per row
+  constexpr int NS = 256 / NC;    // (row, gi) slots per workgroup
+  __shared__ float smax[NS];
+  __shared__ float stot[NS];
+  __shared__ __attribute__((aligned(16))) float sacc[NS][D];
+  const int col = threadIdx.x % NC;
+  const int slot = threadIdx.x / NC;           // rl * ngl + gi
+  const int gi = slot % ngl, rl = slot / ngl;  // (ngl is a power of two)
+  const int rb = NS / ngl;
+  // (a 2-D grid: 65536 workgroups per grid row)
+  const long long row = ((long long)blockIdx.y * 65536 + blockIdx.x) * rb + rl;
+  const bool live = row < rows;
   float mx = -INFINITY;
+  if (live) {
 #pragma unroll 4
-  for (int g = gi; g < nsplit; g += NGL) mx = fmaxf(mx, ws_lse[(long long)g * rows + row]);
-  if (col == 0) smax[gi] = mx;
+    for (int g = gi; g < nsplit; g += ngl) mx = fmaxf(mx, ws_lse[(long long)g * rows + row]);
+  }
+  if (col == 0) smax[slot] = mx;
   __syncthreads();
   mx = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < NGL; ++j) mx = fmaxf(mx, smax[j]);
-  // (mx is finite: every row sees a key of some chunk)
+  for (int j = 0; j < ngl; ++j) mx = fmaxf(mx, smax[rl * ngl + j]);
+  // (mx is finite for a live row: every row sees a key of some chunk)
   float tot = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  if (live) {
 #pragma unroll 4
-  for (int g = gi; g < nsplit; g += NGL) {
-    const float lg = ws_lse[(long long)g * rows + row];
-    const float4 x = *(const float4*)(ws_o + ((long long)g * rows + row) * D + 4 * col);
-    const float wgt = lg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lg - mx) * kLog2e);
-    tot += wgt;
-    a0 = fmaf(wgt, x.x, a0);
-    a1 = fmaf(wgt, x.y, a1);
-    a2 = fmaf(wgt, x.z, a2);
-    a3 = fmaf(wgt, x.w, a3);
+    for (int g = gi; g < nsplit; g += ngl) {
+      const float lg = ws_lse[(long long)g * rows + row];
+      const float4 x = *(const float4*)(ws_o + ((long long)g * rows + row) * D + 4 * col);
+      const float wgt = lg == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((lg - mx) * kLog2e);
+      tot += wgt;
+      a0 = fmaf(wgt, x.x, a0);
+      a1 = fmaf(wgt, x.y, a1);
+      a2 = fmaf(wgt, x.z, a2);
+      a3 = fmaf(wgt, x.w, a3);
+    }
   }
-  if (col == 0) stot[gi] = tot;
-  sacc[gi][4 * col + 0] = a0;
-  sacc[gi][4 * col + 1] = a1;
-  sacc[gi][4 * col + 2] = a2;
-  sacc[gi][4 * col + 3] = a3;
+  if (col == 0) stot[slot] = tot;
+  sacc[slot][4 * col + 0] = a0;
+  sacc[slot][4 * col + 1] = a1;
+  sacc[slot][4 * col + 2] = a2;
+  sacc[slot][4 * col + 3] = a3;
   __syncthreads();
-  if (gi != 0) return;
+  if (gi != 0 || !live) return;
   tot = 0.f;
   a0 = a1 = a2 = a3 = 0.f;
-#pragma unroll
-  for (int j = 0; j < NGL; ++j) {
-    tot += stot[j];
-    a0 += sacc[j][4 * col + 0];
-    a1 += sacc[j][4 * col + 1];
-    a2 += sacc[j][4 * col + 2];
-    a3 += sacc[j][4 * col + 3];
+  for (int j = 0; j < ngl; ++j) {
+    const int sl = rl * ngl + j;
+    tot += stot[sl];
+    a0 += sacc[sl][4 * col + 0];
+    a1 += sacc[sl][4 * col + 1];
+    a2 += sacc[sl][4 * col + 2];
+    a3 += sacc[sl][4 * col + 3];
   }
   const float inv = 1.f / tot;
   bf16x4 ov;
@@ -1040,6 +1097,12 @@ fa_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse
   ov[3] = (__bf16)(a3 * inv);
   *(u32x2*)(o + row * D + 4 * col) = __builtin_bit_cast(u32x2, ov);
   if (col == 0) lse[row] = mx + __logf(tot);
+}
+
+template <int D>
+void launch_merge(float* ws_o, float* ws_lse, void* o, float* lse, long long rows, int G, hipStream_t stream) {
+  hipLaunchKernelGGL(fa_merge_kernel<D>, merge_grid(rows, D, G), dim3(256), 0, stream, ws_o, ws_lse, (uint16_t*)o,
+                     lse, rows, G, merge_ngl(D, G));
 }
 
 // ---------------------------------------------------------------------------
@@ -1342,8 +1405,14 @@ void launch_decode(const void* q, const void* k, const void* v, void* o, float* 
 template <int D, bool CAUSAL>
 void launch_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
                 float c, hipStream_t stream) {
-  dim3 grid((N + F32_BQ - 1) / F32_BQ, B * H);
-  hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL>), grid, dim3(64), 0, stream, q, k, v, o, lse, N, c);
+  // fewer than 512 waves with one query per lane: spread each query over 16 lanes
+  if ((long long)B * H * ((N + 63) / 64) < 512) {
+    dim3 grid((N + 3) / 4, B * H);
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL, 16>), grid, dim3(64), 0, stream, q, k, v, o, lse, N, c);
+  } else {
+    dim3 grid((N + 63) / 64, B * H);
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL, 1>), grid, dim3(64), 0, stream, q, k, v, o, lse, N, c);
+  }
 }
 
 #ifndef FA_D128_BC
@@ -1493,11 +1562,9 @@ extern "C" int fa_fwd_split(const void* q, const void* k, const void* v, void* o
     }
     if (g > 1) {
       if (d == 128)
-        hipLaunchKernelGGL(fa_merge_kernel<128>, merge_grid(rows), dim3(256), 0, stream, ws_o,
-                           ws_lse, (uint16_t*)o, lse, rows, g);
+        launch_merge<128>(ws_o, ws_lse, o, lse, rows, g, stream);
       else
-        hipLaunchKernelGGL(fa_merge_kernel<64>, merge_grid(rows), dim3(256), 0, stream, ws_o,
-                           ws_lse, (uint16_t*)o, lse, rows, g);
+        launch_merge<64>(ws_o, ws_lse, o, lse, rows, g, stream);
     }
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
   }
@@ -1510,8 +1577,7 @@ extern "C" int fa_fwd_split(const void* q, const void* k, const void* v, void* o
     else
       launch_bf16_ex<CfgD128, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream, g, chunk, ws_o,
                                      ws_lse);
-    hipLaunchKernelGGL(fa_merge_kernel<128>, merge_grid(rows), dim3(256), 0, stream, ws_o, ws_lse,
-                       (uint16_t*)o, lse, rows, g);
+    launch_merge<128>(ws_o, ws_lse, o, lse, rows, g, stream);
   } else {
     if (causal)
       launch_bf16_ex<CfgD64, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream, g, chunk, ws_o,
@@ -1519,8 +1585,7 @@ extern "C" int fa_fwd_split(const void* q, const void* k, const void* v, void* o
     else
       launch_bf16_ex<CfgD64, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, off, wnd, c, qsign, stream, g, chunk, ws_o,
                                     ws_lse);
-    hipLaunchKernelGGL(fa_merge_kernel<64>, merge_grid(rows), dim3(256), 0, stream, ws_o, ws_lse,
-                       (uint16_t*)o, lse, rows, g);
+    launch_merge<64>(ws_o, ws_lse, o, lse, rows, g, stream);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -88,6 +88,24 @@ def test_small_shapes(dtype, d, N, causal):
     assert_close(f64(o), f64(lse), o_ref, lse_ref, dtype, f"N={N} d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_f32_large_one_query_per_lane(d, causal):
+    """fp32 at B=2, H=4, N=4096 (512 waves of 64 queries): one query per
+    lane; the small fp32 cases spread each query over 16 lanes.  Sampled
+    rows of two heads against the oracle, fp32 tolerance."""
+    q, k, v = workloads.make_qkv(2, 4, 4096, d, torch.float32, seed=900 + d)
+    say("f32 large", d, causal)
+    o, lse = run_gpu(q, k, v, causal, 1.0 / math.sqrt(d))
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rows = workloads.sample_rows(4096, 96, 900 + d)
+    for b, h in ((0, 0), (1, 3)):
+        o_ref, lse_ref = attention_rows_ref(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), 1.0 / math.sqrt(d), causal,
+                                            rows)
+        idx = torch.as_tensor(rows, device="cuda")
+        assert_close(f64(o[b, h][idx]), f64(lse[b, h][idx]), o_ref, lse_ref, torch.float32, f"b={b} h={h}")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("d", [64, 128])
 def test_worked_example_embedded(dtype, d):
