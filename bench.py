@@ -59,7 +59,16 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak (2.5 PFLOP/s)
 DEFAULT_WORKLOAD = "longctx_n16384_d128_causal"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "io_aware_exact_fa1_amd", "csrc", "fa_fwd.hip")
+# the sources that define the forward kernel (its counters are void once they change)
+KERNEL_SOURCES = [os.path.join(ROOT, "io_aware_exact_fa1_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_device.h")]
+
+
+def kernel_source_sha256():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -112,8 +121,7 @@ def measured_traffic(workload):
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        with open(KERNEL_SOURCE, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_source_sha256()
     except (OSError, ValueError):
         return None
     if t.get("workload") != workload or t.get("kernel_source_sha256") != sha:

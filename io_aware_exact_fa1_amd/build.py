@@ -13,6 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "fa_fwd.hip")
 SRC_BWD = os.path.join(HERE, "csrc", "fa_bwd.hip")
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("fa_fwd.hip", "fa_fwd_f32.hip", "fa_split.hip", "fa_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
@@ -31,7 +32,7 @@ def compile_cmd(out, extra=()):
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
         # packed fp32 VALU ops stay off: plain fp32 ops only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-I", INCLUDE, *extra, SRC, SRC_BWD, "-o", out,
+        "-I", INCLUDE, *extra, *SOURCES, "-o", out,
     ]
 
 
