@@ -213,6 +213,14 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   blane<C>(bl, w, lane);
   const unsigned lbase = (unsigned)(uintptr_t)(const unsigned char LDS_AS*)smem;
   const size_t hoff = (size_t)bh * (size_t)N * C::D;
+  int rowa[C::KB], tra[C::DB][2];
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) rowa[kb] = (int)lbase + bl.row[kb];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    tra[db][0] = (int)lbase + bl.tr[db][0];
+    tra[db][1] = (int)lbase + bl.tr[db][1];
+  }
 
   for (int ti = 0; ti < ntiles; ++ti) {
     const int q0 = tiles[ti] * C::ROWS;
@@ -252,44 +260,67 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
     const uint16_t* kh = k + hoff;
     const uint16_t* vh = v + hoff;
-    auto issue = [&](int j) {
+    auto issue = [&](int j) __attribute__((always_inline)) {
       const unsigned st = lbase + (unsigned)(j & 1) * C::STAGE;
       copy_tile<C>(kh, st, j * C::T, N, bl, w);
       copy_tile<C>(vh, st + C::TB, j * C::T, N, bl, w);
     };
-    issue(0);
-    wait_copies<0>();
-    barrier();
-    for (int j = 0; j < nkv; ++j) {
+    // dP^T starts from -D, so that the accumulator ends as dP^T - D
+    f32x16 negd;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negd[i] = -dval;
+    const unsigned char LDS_AS* lds = (const unsigned char LDS_AS*)0;
+    // One key tile; stage ST and the mask are compile-time, so every LDS
+    // address is a per-lane offset (LDS base folded in) plus an immediate.
+    auto step = [&](int j, auto stc, auto maskc) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stc)::value;
+      constexpr bool MASK = decltype(maskc)::value;
+      constexpr int KT = ST * C::STAGE, VT = KT + C::TB;
       if (j + 1 < nkv) issue(j + 1);
-      const unsigned kt = lbase + (unsigned)(j & 1) * C::STAGE;
-      const unsigned vt = kt + C::TB;
-      // S^T = K Q^T and dP^T = V dO^T (lane: query l%32; regs: keys
+      // S^T = K Q^T and dP^T - D = V dO^T - D (lane: query l%32; regs: keys
       // 8*(r/4) + 4h + r%4)
-      f32x16 s = {}, dp = {};
+      f32x16 s = {}, dp = negd;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        s = mfma(lds_row(kt + bl.row[kb]), qr[kb], s);
-        dp = mfma(lds_row(vt + bl.row[kb]), dor[kb], dp);
+        s = mfma(*(const bf16x8 LDS_AS*)(lds + rowa[kb] + KT), qr[kb], s);
+        dp = mfma(*(const bf16x8 LDS_AS*)(lds + rowa[kb] + VT), dor[kb], dp);
       }
-      const int k0 = j * C::T;
-      const bool mask = j >= nfull;
-      const int lim = (CAUSAL ? min(query, N - 1) : N - 1) - (k0 + 4 * h);
+      const int lim = MASK ? (CAUSAL ? min(query, N - 1) : N - 1) - (j * C::T + 4 * h) : 0;
       bf16x8 dsb[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c, -l2));
-        if (mask && 8 * (i >> 2) + (i & 3) > lim) pv = 0.f;
-        const float dsv = pv * (dp[i] - dval);
-        dsb[i >> 3][i & 7] = (__bf16)dsv;
+        if (MASK && 8 * (i >> 2) + (i & 3) > lim) pv = 0.f;
+        dsb[i >> 3][i & 7] = (__bf16)(pv * dp[i]);
       }
       // dQ^T += K^T dS^T (K^T by transpose reads of the K tile)
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[db] = mfma(lds_tr<C>(bl, kt, kq, db), dsb[kq], acc[db]);
+        for (int db = 0; db < C::DB; ++db) {
+          const int off = KT + kq * 16 * C::ROWB;
+          const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + tra[db][0] + off));
+          const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + tra[db][1] + off));
+          const bf16x8 kt = __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+          acc[db] = mfma(kt, dsb[kq], acc[db]);
+        }
       wait_copies<0>();
       barrier();
+    };
+    issue(0);
+    wait_copies<0>();
+    barrier();
+    int j = 0;
+    for (; j + 1 < nkv; j += 2) {
+      if (j < nfull) step(j, std::integral_constant<int, 0>{}, std::false_type{});
+      else step(j, std::integral_constant<int, 0>{}, std::true_type{});
+      if (j + 1 < nfull) step(j + 1, std::integral_constant<int, 1>{}, std::false_type{});
+      else step(j + 1, std::integral_constant<int, 1>{}, std::true_type{});
+    }
+    if (j < nkv) {
+      if (j < nfull) step(j, std::integral_constant<int, 0>{}, std::false_type{});
+      else step(j, std::integral_constant<int, 0>{}, std::true_type{});
     }
     if (query < N) store_rows<C>(dq + hoff + (size_t)query * C::D, acc, scale, h);
   }
@@ -323,6 +354,18 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   blane<C>(bl, w, lane);
   const unsigned lbase = (unsigned)(uintptr_t)(const unsigned char LDS_AS*)smem;
   const size_t hoff = (size_t)bh * (size_t)N * C::D;
+  // per-lane LDS addresses with the base folded in (streamed tiles: + stage
+  // immediates; the resident V rows of this wave: + a wave-uniform offset)
+  int rowa[C::KB], tra[C::DB][2];
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb) rowa[kb] = (int)lbase + bl.row[kb];
+  const int vw = 2 * C::STAGE + w * C::TB;  // this wave's resident V rows, from the base
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    tra[db][0] = (int)lbase + bl.tr[db][0];
+    tra[db][1] = (int)lbase + bl.tr[db][1];
+  }
+  const int xa = (int)lbase;
   const float* lh = lse + (size_t)bh * N;
   const float* dh = delta + (size_t)bh * N;
 
@@ -342,7 +385,6 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const unsigned vres = lbase + 2 * C::STAGE;
 #pragma unroll
     for (int t = 0; t < C::NW; ++t) copy_tile<C>(v + hoff, vres + t * C::TB, k0 + t * C::T, N, bl, w);
-    const unsigned vmine = vres + w * C::TB;
     f32x16 dka[C::DB], dva[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -360,8 +402,9 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
     const uint16_t* qh = q + hoff;
     const uint16_t* oh = dout + hoff;
-    auto issue = [&](int i) {
-      const unsigned st = lbase + (unsigned)(i & 1) * C::STAGE;
+    // stage of query tile i: (i - qt0) & 1
+    auto issue = [&](int i) __attribute__((always_inline)) {
+      const unsigned st = lbase + (unsigned)((i - qt0) & 1) * C::STAGE;
       copy_tile<C>(qh, st, i * C::T, N, bl, w);
       copy_tile<C>(oh, st + C::TB, i * C::T, N, bl, w);
       if (w == 0) {
@@ -373,58 +416,97 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     issue(qt0);
     wait_copies<0>();
     barrier();
-    for (int i = qt0; i < nq; ++i) {
+    // V rows negated in place (once per key tile), so that dP - D comes out
+    // of the matrix cores as D + dO (-V)^T with the accumulator started at D
+    {
+      unsigned char LDS_AS* vb = (unsigned char LDS_AS*)0 + vres;
+#pragma unroll
+      for (int e = 0; e < C::NW * C::TB / (16 * C::NW * 64); ++e) {
+        u32x4 LDS_AS* p = (u32x4 LDS_AS*)(vb + 16 * (threadIdx.x + C::NW * 64 * e));
+        *p = *p ^ 0x80008000u;
+      }
+    }
+    barrier();
+    const unsigned char LDS_AS* lds = (const unsigned char LDS_AS*)0;
+    // masked: tiles holding the diagonal (before qfull) and a ragged last tile
+    auto masked = [&](int i) __attribute__((always_inline)) { return i < qfull || i * C::T + C::T > N; };
+    // One query tile; stage ST and the mask are compile-time, so every LDS
+    // address is a per-lane offset (LDS base folded in) plus an immediate.
+    auto step = [&](int i, auto stc, auto maskc) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stc)::value;
+      constexpr bool MASK = decltype(maskc)::value;
+      constexpr int QT = ST * C::STAGE, OT = QT + C::TB, XT = QT + 2 * C::TB;
       if (i + 1 < nq) issue(i + 1);
-      const unsigned qt = lbase + (unsigned)(i & 1) * C::STAGE;
-      const unsigned ot = qt + C::TB;
-      // S = Q K^T and dP = dO V^T (lane: key l%32; regs: queries
-      // 8*(r/4) + 4h + r%4 of the tile)
-      f32x16 s = {}, dp = {};
+      // D of this lane's 16 queries starts the dP accumulator
+      f32x16 dp;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 b = *(const f32x4 LDS_AS*)(lds + xa + XT + 128 + (8 * g + 4 * h) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * g + e] = b[e];
+      }
+      // S = Q K^T and D - dP = D + dO (-V)^T (lane: key l%32; regs:
+      // queries 8*(r/4) + 4h + r%4 of the tile)
+      f32x16 s = {};
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        s = mfma(lds_row(qt + bl.row[kb]), kr[kb], s);
-        dp = mfma(lds_row(ot + bl.row[kb]), lds_row(vmine + bl.row[kb]), dp);
+        s = mfma(*(const bf16x8 LDS_AS*)(lds + rowa[kb] + QT), kr[kb], s);
+        dp = mfma(*(const bf16x8 LDS_AS*)(lds + rowa[kb] + OT), *(const bf16x8 LDS_AS*)(lds + rowa[kb] + vw), dp);
       }
-      // L (as log2) and D of this lane's 16 queries
-      float lq[16], dq16[16];
-      {
-        const unsigned char LDS_AS* lds = (const unsigned char LDS_AS*)0;
-        const unsigned xb = qt + 2 * C::TB;
+      // L (as log2) of the lane's 16 queries
+      float lq[16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 a = *(const f32x4 LDS_AS*)(lds + xb + (8 * g + 4 * h) * 4);
-          const f32x4 b = *(const f32x4 LDS_AS*)(lds + xb + 128 + (8 * g + 4 * h) * 4);
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 a = *(const f32x4 LDS_AS*)(lds + xa + XT + (8 * g + 4 * h) * 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lq[4 * g + e] = a[e];
-            dq16[4 * g + e] = b[e];
-          }
+        for (int e = 0; e < 4; ++e) lq[4 * g + e] = a[e];
+      }
+      // register r holds query q0 + 4h + rel, rel = 8*(r/4) + r%4: visible
+      // iff rel <= N - 1 - (q0 + 4h) and (causal) rel >= key - (q0 + 4h)
+      if (masked(i)) {  // wave-uniform: only diagonal and ragged tiles
+        const int qb = i * C::T + 4 * h;
+        const int rhi = N - 1 - qb, rlo = CAUSAL ? key - qb : -1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rel = 8 * (r >> 2) + (r & 3);
+          if (rel > rhi || rel < rlo) s[r] = -INFINITY;
         }
       }
-      const int q0 = i * C::T;
-      const bool mask = i < qfull || q0 + C::T > N;
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qi = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lq[r] * kLog2e));
-        if (mask && (qi >= N || (CAUSAL && qi < key))) pv = 0.f;
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lq[r] * kLog2e));
         pb[r >> 3][r & 7] = (__bf16)pv;
-        dsb[r >> 3][r & 7] = (__bf16)(pv * (dp[r] - dq16[r]));
+        dsb[r >> 3][r & 7] = (__bf16)(pv * dp[r]);  // -dS
       }
-      // dV^T += dO^T P and dK^T += Q^T dS (dO^T and Q^T by transpose reads)
+      // dV^T += dO^T P and -dK^T += Q^T (-dS) (dO^T and Q^T by transpose reads)
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          dva[db] = mfma(lds_tr<C>(bl, ot, kq, db), pb[kq], dva[db]);
-          dka[db] = mfma(lds_tr<C>(bl, qt, kq, db), dsb[kq], dka[db]);
+          const int off = kq * 16 * C::ROWB;
+          const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + tra[db][0] + OT + off));
+          const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + tra[db][1] + OT + off));
+          const i16x4 b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + tra[db][0] + QT + off));
+          const i16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + tra[db][1] + QT + off));
+          const bf16x8 ot = __builtin_shufflevector(__builtin_bit_cast(bf16x4, a0), __builtin_bit_cast(bf16x4, a1),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 qt = __builtin_shufflevector(__builtin_bit_cast(bf16x4, b0), __builtin_bit_cast(bf16x4, b1),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+          dva[db] = mfma(ot, pb[kq], dva[db]);
+          dka[db] = mfma(qt, dsb[kq], dka[db]);
         }
       wait_copies<0>();
       barrier();
+    };
+    int i = qt0;
+    for (; i + 1 < nq; i += 2) {
+      step(i, std::integral_constant<int, 0>{}, std::false_type{});
+      step(i + 1, std::integral_constant<int, 1>{}, std::false_type{});
     }
+    if (i < nq) step(i, std::integral_constant<int, 0>{}, std::false_type{});
     if (key < N) {
-      store_rows<C>(dk + hoff + (size_t)key * C::D, dka, scale, h);
+      store_rows<C>(dk + hoff + (size_t)key * C::D, dka, -scale, h);  // dka holds -dK^T / scale
       store_rows<C>(dv + hoff + (size_t)key * C::D, dva, 1.f, h);
     }
   }
