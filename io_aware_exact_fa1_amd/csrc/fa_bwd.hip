@@ -52,6 +52,8 @@ using namespace fa;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+constexpr int DQ_NST = 3;  // LDS stages of the dQ kernel's K/V ring
+
 // Tile configuration of both backward kernels.
 template <int D_>
 struct BCfg {
@@ -69,6 +71,7 @@ struct BCfg {
   static constexpr int NI = NINST / NW;     // ... per wave
   static constexpr int XB = 1024;           // room for the L and D rows of a query tile (256 B)
   static constexpr int STAGE = 2 * TB + XB; // one LDS stage: two matrices (+ L, D)
+  static constexpr int DQSTAGE = 2 * TB;    // one stage of the dQ kernel: K and V
   static_assert(NINST % NW == 0 && NI >= 1, "copies must split evenly over the waves");
   static_assert((NW * RPI) % 16 == 0, "a wave's copy rows must be a swizzle period apart");
 };
@@ -195,8 +198,9 @@ __global__ void __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu
 fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                  const uint16_t* __restrict__ o, const float* __restrict__ lse, const uint16_t* __restrict__ dout,
                  uint16_t* __restrict__ dq, float* __restrict__ delta, int N, int T_r, int units_per_head,
-                 int num_units, int per_xcd, float c, float scale) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
+                 int num_units, int per_xcd, float c, float scale, unsigned ssign) {
+  // a ring of DQ_NST stages of (K, V) tiles: copies run two tiles ahead
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[DQ_NST * C::DQSTAGE];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31;
@@ -235,7 +239,7 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const size_t ro = hoff + (size_t)qrow * C::D + 8 * h;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        qr[kb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q + ro + 16 * kb));
+        qr[kb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q + ro + 16 * kb) ^ ssign);
         dor[kb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(dout + ro + 16 * kb));
         const bf16x8 ov = __builtin_bit_cast(bf16x8, *(const u32x4*)(o + ro + 16 * kb));
 #pragma unroll
@@ -261,7 +265,7 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* kh = k + hoff;
     const uint16_t* vh = v + hoff;
     auto issue = [&](int j) __attribute__((always_inline)) {
-      const unsigned st = lbase + (unsigned)(j & 1) * C::STAGE;
+      const unsigned st = lbase + (unsigned)(j % DQ_NST) * C::DQSTAGE;
       copy_tile<C>(kh, st, j * C::T, N, bl, w);
       copy_tile<C>(vh, st + C::TB, j * C::T, N, bl, w);
     };
@@ -270,13 +274,12 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < 16; ++i) negd[i] = -dval;
     const unsigned char LDS_AS* lds = (const unsigned char LDS_AS*)0;
-    // One key tile; stage ST and the mask are compile-time, so every LDS
-    // address is a per-lane offset (LDS base folded in) plus an immediate.
-    auto step = [&](int j, auto stc, auto maskc) __attribute__((always_inline)) {
+    // One key tile in stage ST (compile-time, so that every LDS address is a
+    // per-lane offset with the LDS base folded in, plus an immediate).
+    auto step = [&](int j, auto stc) __attribute__((always_inline)) {
       constexpr int ST = decltype(stc)::value;
-      constexpr bool MASK = decltype(maskc)::value;
-      constexpr int KT = ST * C::STAGE, VT = KT + C::TB;
-      if (j + 1 < nkv) issue(j + 1);
+      constexpr int KT = ST * C::DQSTAGE, VT = KT + C::TB;
+      if (j + 2 < nkv) issue(j + 2);
       // S^T = K Q^T and dP^T - D = V dO^T - D (lane: query l%32; regs: keys
       // 8*(r/4) + 4h + r%4)
       f32x16 s = {}, dp = negd;
@@ -285,14 +288,17 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         s = mfma(*(const bf16x8 LDS_AS*)(lds + rowa[kb] + KT), qr[kb], s);
         dp = mfma(*(const bf16x8 LDS_AS*)(lds + rowa[kb] + VT), dor[kb], dp);
       }
-      const int lim = MASK ? (CAUSAL ? min(query, N - 1) : N - 1) - (j * C::T + 4 * h) : 0;
+      // a masked score becomes -inf: weight exp2(-inf) = 0 exactly (c > 0)
+      if (j >= nfull) {  // wave-uniform: the diagonal and ragged tiles only
+        const int lim = (CAUSAL ? min(query, N - 1) : N - 1) - (j * C::T + 4 * h);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + (i & 3) > lim) s[i] = -INFINITY;
+      }
       bf16x8 dsb[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = __builtin_amdgcn_exp2f(fmaf(s[i], c, -l2));
-        if (MASK && 8 * (i >> 2) + (i & 3) > lim) pv = 0.f;
-        dsb[i >> 3][i & 7] = (__bf16)(pv * dp[i]);
-      }
+      for (int i = 0; i < 16; ++i)
+        dsb[i >> 3][i & 7] = (__bf16)(__builtin_amdgcn_exp2f(fmaf(s[i], c, -l2)) * dp[i]);
       // dQ^T += K^T dS^T (K^T by transpose reads of the K tile)
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq)
@@ -305,23 +311,28 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                     0, 1, 2, 3, 4, 5, 6, 7);
           acc[db] = mfma(kt, dsb[kq], acc[db]);
         }
-      wait_copies<0>();
+      // tile j + 1 has landed (tile j + 2 may still be in flight); the
+      // barrier also ends every read of stage ST before it is refilled
+      if (j + 2 < nkv) wait_copies<2 * C::NI>();
+      else wait_copies<0>();
       barrier();
     };
     issue(0);
-    wait_copies<0>();
+    if (1 < nkv) {
+      issue(1);
+      wait_copies<2 * C::NI>();
+    } else {
+      wait_copies<0>();
+    }
     barrier();
     int j = 0;
-    for (; j + 1 < nkv; j += 2) {
-      if (j < nfull) step(j, std::integral_constant<int, 0>{}, std::false_type{});
-      else step(j, std::integral_constant<int, 0>{}, std::true_type{});
-      if (j + 1 < nfull) step(j + 1, std::integral_constant<int, 1>{}, std::false_type{});
-      else step(j + 1, std::integral_constant<int, 1>{}, std::true_type{});
+    for (; j + 2 < nkv; j += 3) {
+      step(j, std::integral_constant<int, 0>{});
+      step(j + 1, std::integral_constant<int, 1>{});
+      step(j + 2, std::integral_constant<int, 2>{});
     }
-    if (j < nkv) {
-      if (j < nfull) step(j, std::integral_constant<int, 0>{}, std::false_type{});
-      else step(j, std::integral_constant<int, 0>{}, std::true_type{});
-    }
+    if (j < nkv) step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nkv) step(j + 1, std::integral_constant<int, 1>{});
     if (query < N) store_rows<C>(dq + hoff + (size_t)query * C::D, acc, scale, h);
   }
 }
@@ -334,7 +345,7 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    const uint16_t* __restrict__ v, const float* __restrict__ lse,
                    const uint16_t* __restrict__ dout, const float* __restrict__ delta, uint16_t* __restrict__ dk,
                    uint16_t* __restrict__ dv, int N, int T_r, int units_per_head, int num_units, int per_xcd,
-                   float c, float scale) {
+                   float c, float scale, unsigned ssign) {
   // two stages of (Q, dO, L, D) tiles, then the V rows of the workgroup's keys
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE + C::ROWS * C::ROWB];
   const int lane = threadIdx.x & 63;
@@ -380,7 +391,8 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     {
       const size_t ro = hoff + (size_t)krow * C::D + 8 * h;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) kr[kb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(k + ro + 16 * kb));
+      for (int kb = 0; kb < C::KB; ++kb)
+        kr[kb] = __builtin_bit_cast(bf16x8, *(const u32x4*)(k + ro + 16 * kb) ^ ssign);
     }
     const unsigned vres = lbase + 2 * C::STAGE;
 #pragma unroll
@@ -463,7 +475,10 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       }
       // register r holds query q0 + 4h + rel, rel = 8*(r/4) + r%4: visible
       // iff rel <= N - 1 - (q0 + 4h) and (causal) rel >= key - (q0 + 4h)
+      // a masked score becomes -inf: weight exp2(-inf) = 0 exactly (c > 0)
       if (masked(i)) {  // wave-uniform: only diagonal and ragged tiles
+        // register r holds query q0 + 4h + rel, rel = 8*(r/4) + r%4: visible
+        // iff rel <= N - 1 - (q0 + 4h) and (causal) rel >= key - (q0 + 4h)
         const int qb = i * C::T + 4 * h;
         const int rhi = N - 1 - qb, rlo = CAUSAL ? key - qb : -1;
 #pragma unroll
@@ -552,7 +567,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
 template <class C, bool CAUSAL>
 void launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                 void* dq, void* dk, void* dv, float* delta, int B, int H, int N, float c, float scale,
-                hipStream_t stream) {
+                unsigned ssign, hipStream_t stream) {
   const int T = (N + C::ROWS - 1) / C::ROWS;
   const int units_per_head = CAUSAL ? (T + 1) / 2 : T;
   const int num_units = B * H * units_per_head;
@@ -561,11 +576,11 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* o, cons
   hipLaunchKernelGGL((fa_bwd_dq_kernel<C, CAUSAL>), dim3(grid), dim3(C::NW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, lse,
                      (const uint16_t*)dout, (uint16_t*)dq, delta, N, T, units_per_head, num_units, per_xcd, c,
-                     scale);
+                     scale, ssign);
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<C, CAUSAL>), dim3(grid), dim3(C::NW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, lse, (const uint16_t*)dout,
                      (const float*)delta, (uint16_t*)dk, (uint16_t*)dv, N, T, units_per_head, num_units, per_xcd,
-                     c, scale);
+                     c, scale, ssign);
 }
 
 }  // namespace
@@ -583,13 +598,24 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scale);
   if (st != FA_OK) return st;
   if ((long long)B * H * N == 0) return FA_OK;
-  const float c = scale * kLog2e;
+  // The scores are formed as |scale| * (sign(scale) Q) K^T: the dQ kernel
+  // flips the sign bits of its register Q rows, the dK/dV kernel those of
+  // its register K rows (exact), so that the kernels see c > 0 (a masked
+  // score of -inf then has weight exactly 0).  dQ and dK keep the signed
+  // scale.  A zero scale runs as 2^-100, as in the forward (every
+  // exponent argument rounds to -L log2(e), i.e. P = exp(-L)).
+  const unsigned ssign = (scale < 0.f) ? 0x80008000u : 0u;
+  const float c = scale == 0.f ? 0x1p-100f : fabsf(scale) * kLog2e;
   if (d == 128) {
-    if (causal) launch_bwd<BCfg<128>, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, c, scale, stream);
-    else launch_bwd<BCfg<128>, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, c, scale, stream);
+    if (causal)
+      launch_bwd<BCfg<128>, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, c, scale, ssign, stream);
+    else
+      launch_bwd<BCfg<128>, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, c, scale, ssign, stream);
   } else {
-    if (causal) launch_bwd<BCfg<64>, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, c, scale, stream);
-    else launch_bwd<BCfg<64>, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, c, scale, stream);
+    if (causal)
+      launch_bwd<BCfg<64>, true>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, c, scale, ssign, stream);
+    else
+      launch_bwd<BCfg<64>, false>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, c, scale, ssign, stream);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

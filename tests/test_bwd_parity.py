@@ -160,3 +160,24 @@ def test_bwd_key_shift_and_value_sums():
         tot = np.abs(dv[0, h]).sum(axis=0).max()
         assert np.max(np.abs(dv[0, h].sum(axis=0) - ref_dv_sum)) <= 2e-2 * tot
         assert np.max(np.abs(dk[0, h].sum(axis=0))) <= 2e-2 * np.abs(dk[0, h]).sum(axis=0).max()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.3])
+def test_bwd_scale_variants(scale, d, causal):
+    """Negative scale (the kernels flip the sign of Q or K and run with
+    |scale|), zero scale (uniform weights) and a larger one; ragged N so that
+    diagonal and tail tiles are masked."""
+    require_gpu()
+    N = 200
+    q, k, v, do = _inputs(1, 2, N, d, causal, seed=int(1000 * scale) + d + 31)
+    tag = f"scale={scale} d={d} causal={causal}"
+    say(f"[bwd] {tag}")
+    dq, dk, dv, _, _ = _run(q, k, v, do, causal, scale=scale)
+    q, k, v, do = (f64(x) for x in (q, k, v, do))
+    for h in range(2):
+        rq, rk, rv, _ = attention_bwd_ref(q[0, h], k[0, h], v[0, h], do[0, h], scale, causal)
+        _check("dQ", dq[0, h], rq, f"{tag} h={h}")
+        _check("dK", dk[0, h], rk, f"{tag} h={h}")
+        _check("dV", dv[0, h], rv, f"{tag} h={h}")
