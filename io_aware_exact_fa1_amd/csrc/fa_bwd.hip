@@ -52,7 +52,7 @@ using namespace fa;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int DQ_NST = 3;  // LDS stages of the dQ kernel's K/V ring
+constexpr int DQ_NST = 4;  // LDS stages of the dQ kernel's K/V ring
 
 // Tile configuration of both backward kernels.
 template <int D_>
@@ -274,8 +274,28 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < 16; ++i) negd[i] = -dval;
     const unsigned char LDS_AS* lds = (const unsigned char LDS_AS*)0;
-    // One key tile in stage ST (compile-time, so that every LDS address is a
-    // per-lane offset with the LDS base folded in, plus an immediate).
+    // dQ^T += K^T dS^T for the tile in stage ST (K^T by transpose reads)
+    auto dq_mfma = [&](auto stc, const bf16x8 (&dsb)[2]) __attribute__((always_inline)) {
+      constexpr int KT = decltype(stc)::value * C::DQSTAGE;
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const int off = KT + kq * 16 * C::ROWB;
+          const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + tra[db][0] + off));
+          const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + tra[db][1] + off));
+          const bf16x8 kt = __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+          acc[db] = mfma(kt, dsb[kq], acc[db]);
+        }
+    };
+    // Step j (stage ST = j % 4, compile-time, so that every LDS address is a
+    // per-lane offset with the LDS base folded in, plus an immediate): the
+    // products of tile j (S^T, dP^T) together with the dQ product of tile
+    // j - 1, whose dS^T the previous step left in dsp; then the softmax
+    // gradient of tile j into dsp.  Copies run two tiles ahead; a stage is
+    // refilled only after the step that last read it (dQ of its tile).
+    bf16x8 dsp[2];
     auto step = [&](int j, auto stc) __attribute__((always_inline)) {
       constexpr int ST = decltype(stc)::value;
       constexpr int KT = ST * C::DQSTAGE, VT = KT + C::TB;
@@ -288,6 +308,7 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         s = mfma(*(const bf16x8 LDS_AS*)(lds + rowa[kb] + KT), qr[kb], s);
         dp = mfma(*(const bf16x8 LDS_AS*)(lds + rowa[kb] + VT), dor[kb], dp);
       }
+      if (j > 0) dq_mfma(std::integral_constant<int, (ST + DQ_NST - 1) % DQ_NST>{}, dsp);
       // a masked score becomes -inf: weight exp2(-inf) = 0 exactly (c > 0)
       if (j >= nfull) {  // wave-uniform: the diagonal and ragged tiles only
         const int lim = (CAUSAL ? min(query, N - 1) : N - 1) - (j * C::T + 4 * h);
@@ -295,24 +316,11 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int i = 0; i < 16; ++i)
           if (8 * (i >> 2) + (i & 3) > lim) s[i] = -INFINITY;
       }
-      bf16x8 dsb[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        dsb[i >> 3][i & 7] = (__bf16)(__builtin_amdgcn_exp2f(fmaf(s[i], c, -l2)) * dp[i]);
-      // dQ^T += K^T dS^T (K^T by transpose reads of the K tile)
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq)
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const int off = KT + kq * 16 * C::ROWB;
-          const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + tra[db][0] + off));
-          const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS*)(lds + tra[db][1] + off));
-          const bf16x8 kt = __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b),
-                                                    0, 1, 2, 3, 4, 5, 6, 7);
-          acc[db] = mfma(kt, dsb[kq], acc[db]);
-        }
+        dsp[i >> 3][i & 7] = (__bf16)(__builtin_amdgcn_exp2f(fmaf(s[i], c, -l2)) * dp[i]);
       // tile j + 1 has landed (tile j + 2 may still be in flight); the
-      // barrier also ends every read of stage ST before it is refilled
+      // barrier also orders every read of this step before later refills
       if (j + 2 < nkv) wait_copies<2 * C::NI>();
       else wait_copies<0>();
       barrier();
@@ -326,13 +334,22 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     barrier();
     int j = 0;
-    for (; j + 2 < nkv; j += 3) {
+    for (; j + 3 < nkv; j += 4) {
       step(j, std::integral_constant<int, 0>{});
       step(j + 1, std::integral_constant<int, 1>{});
       step(j + 2, std::integral_constant<int, 2>{});
+      step(j + 3, std::integral_constant<int, 3>{});
     }
-    if (j < nkv) step(j, std::integral_constant<int, 0>{});
-    if (j + 1 < nkv) step(j + 1, std::integral_constant<int, 1>{});
+    // the remaining tiles, then the dQ product of the last one
+    const int rem = nkv - j;
+    if (rem > 0) step(j, std::integral_constant<int, 0>{});
+    if (rem > 1) step(j + 1, std::integral_constant<int, 1>{});
+    if (rem > 2) step(j + 2, std::integral_constant<int, 2>{});
+    if (rem == 0) dq_mfma(std::integral_constant<int, 3>{}, dsp);
+    else if (rem == 1) dq_mfma(std::integral_constant<int, 0>{}, dsp);
+    else if (rem == 2) dq_mfma(std::integral_constant<int, 1>{}, dsp);
+    else dq_mfma(std::integral_constant<int, 2>{}, dsp);
+    barrier();  // every wave is done with the ring before the next tile refills it
     if (query < N) store_rows<C>(dq + hoff + (size_t)query * C::D, acc, scale, h);
   }
 }
