@@ -40,7 +40,8 @@
 //    immediate, so that phase issues no vector-ALU work at all.
 //  * The exponent reference of a row is fixed after its first key tile
 //    (no rescaling of acc in the loop); rows whose scores later jump too
-//    far above it are redone by a second, exact-rescaling kernel.
+//    far above it are redone, by the same workgroup right after its fast
+//    pass, with exact rescaling (one launch per call).
 //  * Exponentials are exp2 with log2(e) folded into the scale; m, l and the
 //    output accumulator stay in fp32 registers; O is divided by l once.
 //  * Work units are query tiles (causal: a heavy tile paired with a light
@@ -76,7 +77,7 @@ using namespace fa;
 // arithmetic (the recurrence holds for any common reference; the running
 // max only bounds the exponents).  A row whose tile sum exceeds the bound
 // (a score jumped more than kSlack above the reference, or overflowed to
-// +inf) is marked (NaN LSE) and recomputed by the exact-rescaling kernel.
+// +inf) is marked (NaN LSE) and recomputed by the exact-rescaling pass.
 constexpr float kSlack = 48.0f;
 constexpr float kJumpSum = 0x1p48f;  // 2^kSlack
 
@@ -289,7 +290,7 @@ __device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& l
 // kernel): every tile computes its row max, and the reference is the max
 // of the first tile in which the row sees a key; MASK then also applies the
 // sliding window's lower bound when wnd > 0.
-// EXACT = true (recompute kernel): m is the running max and l and acc are
+// EXACT = true (recompute pass): m is the running max and l and acc are
 // rescaled by exp2(m_old - m_new) on every tile.
 template <class C, bool CAUSAL, bool MASK, bool EXACT, bool FIRST, bool MAXALL = false>
 __device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB],
@@ -395,17 +396,16 @@ struct ExtArgs {
   float* ws_lse;
 };
 
-// EXACT = false: the fast kernel over every query tile.  EXACT = true: the
-// recompute kernel, which only redoes the query rows the fast kernel marked
-// (NaN LSE) and is a no-op for tiles without a marked row.
-template <class C, bool CAUSAL, bool EXACT, bool EXT = false>
-__global__ void __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                   const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-                   int N, int T_r, int units_per_head, int num_units, int per_xcd, float c,
-                   unsigned int qsign, ExtArgs ex) {
-  // the K/V ring, then one flag per wave (recompute kernel)
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDSB + 4 * C::NW];
+// One work unit.  EXACT = false: the fast pass over the unit's query
+// tiles; returns (workgroup-uniform) whether it marked a row (NaN LSE).
+// EXACT = true: the recompute pass, which only redoes the query rows marked
+// (NaN LSE) and skips tiles without a marked row.  smem: the K/V ring, then
+// one flag per wave.
+template <class C, bool CAUSAL, bool EXACT, bool EXT>
+__device__ __attribute__((always_inline)) inline bool
+fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+         uint16_t* __restrict__ o, float* __restrict__ lse, int N, int T_r, int units_per_head, int num_units,
+         int per_xcd, float c, unsigned int qsign, const ExtArgs& ex, unsigned char LDS_AS* smem) {
   int LDS_AS* wave_marked = (int LDS_AS*)(smem + C::LDSB);
 
   const int lane = threadIdx.x & 63;
@@ -416,7 +416,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   // Workgroups are dispatched round-robin over the 8 XCDs: block b runs on
   // XCD b % 8.  Give XCD x the contiguous units [x*per_xcd, (x+1)*per_xcd).
   const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (u >= num_units) return;
+  if (u >= num_units) return false;
   const int bh = u / units_per_head;
   const int ur = u - bh * units_per_head;
   int tiles[2];
@@ -440,7 +440,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   }
 
   LaneOffsets<C> lo;
-  lane_offsets<C>(lo, (unsigned)(uintptr_t)(const unsigned char LDS_AS*)smem, w, lane);
+  lane_offsets<C>(lo, (unsigned)(uintptr_t)smem, w, lane);
 
   const size_t hoff = (size_t)bh * (size_t)Nq * C::D;
   // EXT: query head h of batch b reads K/V head h / group (the index is
@@ -457,13 +457,14 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int qoff = (EXT && CAUSAL) ? ex.offset : 0;   // position of query row 0
   const int wnd = (EXT && CAUSAL) ? ex.window : 0;    // sliding window (0: none)
 
+  bool unit_jumped = false;  // fast pass: a row of this wave was marked
   for (int ti = 0; ti < ntiles; ++ti) {
     // (EXT: said to be wave-uniform, so that the addresses derived from it
     // stay scalar)
     const int q0 = EXT ? __builtin_amdgcn_readfirstlane(tiles[ti] * C::BR) : tiles[ti] * C::BR;
     const int qw0 = q0 + w * 32;
 
-    bool mine = false;  // recompute kernel: this lane's row was marked
+    bool mine = false;  // recompute pass: this lane's row was marked
     if (EXACT) {
       const int query = qw0 + l32;
       if (query < Nq) {
@@ -768,6 +769,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const float lt = half_sum(lsum);
     // a row is marked when either half of its keys flagged a jump
     jumped = half_max(jumped ? 1.f : 0.f) != 0.f;
+    unit_jumped |= jumped;
     // (split-KV: no visible key in this chunk -> O_g = 0, LSE_g = -inf)
     const bool empty = EXT && !(lt > 0.f);
     const float inv = empty ? 0.f : 1.f / lt;
@@ -788,7 +790,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
       if (h == 0)
         ex.ws_lse[prow] = jumped ? __builtin_nanf("") : (empty ? -INFINITY : (m + __log2f(lt)) * kLn2);
-    } else if (query < Nq && (!EXACT || mine)) {  // the recompute kernel stores only marked rows
+    } else if (query < Nq && (!EXACT || mine)) {  // the recompute pass stores only marked rows
       uint16_t* orow = o + hoff + (size_t)query * C::D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -800,9 +802,40 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           *(u32x2*)(orow + 32 * db + 8 * a + 4 * h) = __builtin_bit_cast(u32x2, ov);
         }
       // a row whose scores jumped past the fixed reference is marked (NaN
-      // LSE) for the recompute kernel
+      // LSE) for the recompute pass
       if (h == 0) lse[(size_t)bh * Nq + query] = jumped ? __builtin_nanf("") : (m + __log2f(lt)) * kLn2;
     }
+  }
+  if (EXACT) return false;
+  // any row of the unit marked? (the flags are rewritten only after this
+  // barrier, by the recompute pass)
+  if (lane == 0) wave_marked[w] = __builtin_amdgcn_ballot_w64(unit_jumped) != 0;
+  __syncthreads();
+  int any = 0;
+#pragma unroll
+  for (int ww = 0; ww < C::NW; ++ww) any |= wave_marked[ww];
+  return __builtin_amdgcn_readfirstlane(any) != 0;
+}
+
+// The forward kernel: the fast pass over one work unit, then -- only when it
+// marked a row, i.e. a row whose scores jumped past its fixed exponent
+// reference -- the exact recompute pass over the same unit, in the same
+// workgroup.  The marks are read back from LSE after a workgroup barrier,
+// which makes the fast pass's global stores visible to every wave of the
+// workgroup.
+template <class C, bool CAUSAL, bool EXT = false>
+__global__ void __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                   const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
+                   int N, int T_r, int units_per_head, int num_units, int per_xcd, float c,
+                   unsigned int qsign, ExtArgs ex) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDSB + 4 * C::NW];
+  unsigned char LDS_AS* lds = (unsigned char LDS_AS*)smem;
+  if (fwd_unit<C, CAUSAL, false, EXT>(q, k, v, o, lse, N, T_r, units_per_head, num_units, per_xcd, c, qsign, ex,
+                                      lds)) {
+    __syncthreads();
+    fwd_unit<C, CAUSAL, true, EXT>(q, k, v, o, lse, N, T_r, units_per_head, num_units, per_xcd, c, qsign, ex,
+                                   lds);
   }
 }
 
@@ -843,13 +876,7 @@ void launch_bf16(const void* q, const void* k, const void* v, void* o, float* ls
   const int num_units = B * H * units_per_head;
   const int per_xcd = (num_units + 7) / 8;
   const int grid = per_xcd * 8;
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, false>), dim3(grid), dim3(C::NW * 64), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, T_r,
-                     units_per_head, num_units, per_xcd, c, qsign, ExtArgs{});
-  // Waves marked by the fast kernel are redone with exact rescaling; the
-  // launch is ordered after the fast kernel on the stream and its
-  // workgroups exit at once when nothing is marked.
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, true>), dim3(grid), dim3(C::NW * 64), 0, stream,
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL>), dim3(grid), dim3(C::NW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, T_r,
                      units_per_head, num_units, per_xcd, c, qsign, ExtArgs{});
 }
@@ -866,10 +893,7 @@ void launch_bf16_ex(const void* q, const void* k, const void* v, void* o, float*
   const int per_xcd = (num_units + 7) / 8;
   const int grid = per_xcd * 8;
   const ExtArgs ex{T, S, Hq, Hq / Hkv, offset, window, pair, nsplit, chunk, B * Hq, ws_o, ws_lse};
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, false, true>), dim3(grid), dim3(C::NW * 64), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, T, T_r,
-                     units_per_head, num_units, per_xcd, c, qsign, ex);
-  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, true, true>), dim3(grid), dim3(C::NW * 64), 0, stream,
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL, true>), dim3(grid), dim3(C::NW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, T, T_r,
                      units_per_head, num_units, per_xcd, c, qsign, ex);
 }
