@@ -33,14 +33,16 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 template <int D, bool CAUSAL, int KL>
 __global__ void __launch_bounds__(64)
 fa_fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-                  float* __restrict__ o, float* __restrict__ lse, int N, float c) {
+                  float* __restrict__ o, float* __restrict__ lse, int N, long long BH, float c) {
   constexpr int QW = 64 / KL;  // queries per wave
+  // (b, h) from the y and z grid indices (each at most 65535)
+  const long long bh = (long long)blockIdx.z * 65535 + blockIdx.y;
+  if (bh >= BH) return;
   __shared__ float ks[F32_BK][D];
   __shared__ float vs[F32_BK][D];
   const int t = threadIdx.x;
   const int qi = t / KL, kl = t % KL;
   const int q0 = blockIdx.x * QW;
-  const int bh = blockIdx.y;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const int query = q0 + qi;
   const int qrow = min(query, N - 1);
@@ -136,12 +138,14 @@ template <int D, bool CAUSAL>
 void launch_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
                 float c, hipStream_t stream) {
   // fewer than 512 waves with one query per lane: spread each query over 16 lanes
-  if ((long long)B * H * ((N + 63) / 64) < 512) {
-    dim3 grid((N + 3) / 4, B * H);
-    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL, 16>), grid, dim3(64), 0, stream, q, k, v, o, lse, N, c);
+  const long long bh = (long long)B * H;
+  const unsigned gy = (unsigned)(bh < 65535 ? bh : 65535), gz = (unsigned)((bh + 65534) / 65535);
+  if (bh * ((N + 63) / 64) < 512) {
+    dim3 grid((N + 3) / 4, gy, gz);
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL, 16>), grid, dim3(64), 0, stream, q, k, v, o, lse, N, bh, c);
   } else {
-    dim3 grid((N + 63) / 64, B * H);
-    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL, 1>), grid, dim3(64), 0, stream, q, k, v, o, lse, N, c);
+    dim3 grid((N + 63) / 64, gy, gz);
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<D, CAUSAL, 1>), grid, dim3(64), 0, stream, q, k, v, o, lse, N, bh, c);
   }
 }
 
