@@ -181,3 +181,20 @@ def test_bwd_scale_variants(scale, d, causal):
         _check("dQ", dq[0, h], rq, f"{tag} h={h}")
         _check("dK", dk[0, h], rk, f"{tag} h={h}")
         _check("dV", dv[0, h], rv, f"{tag} h={h}")
+
+
+def test_bwd_many_heads_short_rows():
+    """B = 8, H = 32, N = 129 (causal): 256 heads of two key tiles (one of a
+    single row); every 17th head against the oracle."""
+    require_gpu()
+    q, k, v, do = _inputs(8, 32, 129, 128, True, seed=4242)
+    say("[bwd] many heads")
+    dq, dk, dv, _, _ = _run(q, k, v, do, True)
+    q, k, v, do = (f64(x) for x in (q, k, v, do))
+    scale = 1.0 / np.sqrt(128)
+    for idx in range(0, 8 * 32, 17):
+        b, h = divmod(idx, 32)
+        rq, rk, rv, _ = attention_bwd_ref(q[b, h], k[b, h], v[b, h], do[b, h], scale, True)
+        _check("dQ", dq[b, h], rq, f"b={b} h={h}")
+        _check("dK", dk[b, h], rk, f"b={b} h={h}")
+        _check("dV", dv[b, h], rv, f"b={b} h={h}")

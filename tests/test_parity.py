@@ -198,3 +198,22 @@ def test_score_jump_recompute(d, causal):
     o, lse = run_gpu(q, k, v, causal, scale)
     o_ref, lse_ref = attention_ref(f64(q), f64(k), f64(v), scale, causal)
     assert_close(f64(o), f64(lse), o_ref, lse_ref, torch.bfloat16, f"jump d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_heads_short_rows(d, causal):
+    """B = 16, H = 64, N = 65: 1024 heads of one full and one one-row query
+    tile each, so the work units far outnumber the CUs and the XCD-remapped
+    grid has a ragged last slice; every 37th head against the oracle, and
+    every head finite."""
+    q, k, v = workloads.make_qkv(16, 64, 65, d, torch.bfloat16, seed=700 + d)
+    say("many heads", d, causal)
+    o, lse = run_gpu(q, k, v, causal, 1.0 / math.sqrt(d))
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    for idx in range(0, 16 * 64, 37):
+        b, h = divmod(idx, 64)
+        o_ref, lse_ref = attention_ref(f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, h:h + 1]), f64(v[b:b + 1, h:h + 1]),
+                                       1.0 / math.sqrt(d), causal)
+        assert_close(f64(o[b:b + 1, h:h + 1]), f64(lse[b:b + 1, h:h + 1]), o_ref, lse_ref, torch.bfloat16,
+                     f"b={b} h={h}")

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from gpu_util import assert_close, f64, require_gpu, say
-from oracle.variants import attention_ex_ref, attention_split_ref, merge_partials_ref
+from oracle.variants import attention_ex_ref, attention_ex_rows_ref, attention_split_ref, merge_partials_ref
 import io_aware_exact_fa1_amd as fa
 
 pytestmark = pytest.mark.gpu
@@ -194,3 +194,21 @@ def test_long_context_chunked_prefill_window():
     require_gpu()
     q, k, v = _qkv(1, 64, 8, 256, 16384, 128, seed=77)
     _check(q, k, v, True, None, 4096, 8, "long prefill window", partials=False)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_many_groups(d):
+    """B = 8 sequences, 64 query heads over 4 K/V heads (groups of 16, so
+    32 columns at T = 2), S = 3000, several chunks: 8 * 4 * G workgroups of
+    the small-tile kernel; every 9th head against the oracle."""
+    require_gpu()
+    B, Hq, Hkv, T, S = 8, 64, 4, 2, 3000
+    q, k, v = _qkv(B, Hq, Hkv, T, S, d, seed=5150 + d)
+    say(f"decode many groups d={d}")
+    o, lse, _, _ = _run(q, k, v, True, None, 0, 6)
+    scale = 1.0 / np.sqrt(d)
+    for idx in range(0, B * Hq, 9):
+        b, h = divmod(idx, Hq)
+        ro, rl = attention_ex_rows_ref(f64(q[b, h]), f64(k[b, h // (Hq // Hkv)]), f64(v[b, h // (Hq // Hkv)]), scale,
+                                       True, S - T, 0, np.arange(T))
+        assert_close(o[b, h], lse[b, h], ro, rl, torch.bfloat16, f"b={b} h={h}")
