@@ -167,6 +167,19 @@ def fa_check_args(q, k, v, o, lse, B, H, N, d, scale, causal, elem_bytes):
                                         int(N), int(d), float(scale), int(causal), int(elem_bytes))
 
 
+def _one_device(*ts):
+    dev = ts[0].device
+    if any(t.device != dev for t in ts):
+        raise ValueError("all tensors must be on one GPU")
+
+
+def _check_out(t, shape, dtype, device, name):
+    """A caller-supplied output buffer must be exactly what the C entry point
+    writes: it trusts the buffer sizes it is given."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}")
+
+
 def forward(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
     """Allocate O / LSE with torch (if not given), call the C entry point for
     the dtype of q, raise FaError on a nonzero status; returns (O, LSE).
@@ -181,14 +194,19 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
         raise ValueError("q, k and v must share one [B, H, N, d] shape")
     if q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k and v must share one dtype")
+    _one_device(q, k, v)
     B, H, N, d = q.shape
     q, k, v = (x.contiguous() for x in (q, k, v))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out(out, q.shape, q.dtype, q.device, "out")
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_out(lse, (B, H, N), torch.float32, q.device, "lse")
     with torch.cuda.device(q.device):
         if q.dtype == torch.bfloat16:
             st = fa_fwd(q, k, v, out, lse, B, H, N, d, scale, causal, stream)
@@ -217,6 +235,7 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, stream=None):
         raise ValueError("all tensors must be GPU tensors")
     if any(x.shape != q.shape for x in ts) or q.dim() != 4:
         raise ValueError("q, k, v, o and dout must share one [B, H, N, d] shape")
+    _one_device(*ts, lse)
     if any(x.dtype != torch.bfloat16 for x in ts) or lse.dtype != torch.float32:
         raise ValueError("q, k, v, o, dout must be bfloat16 and lse float32")
     B, H, N, d = q.shape
@@ -250,6 +269,7 @@ def forward_ex(q, k, v, causal=False, scale=None, offset=None, window=0, stream=
         raise ValueError("q, k and v must share B and d")
     if any(x.dtype != torch.bfloat16 for x in (q, k, v)):
         raise ValueError("fa_fwd_ex takes bfloat16 tensors")
+    _one_device(q, k, v)
     B, Hq, T, d = q.shape
     Hkv, S = k.shape[1], k.shape[2]
     q, k, v = (x.contiguous() for x in (q, k, v))
@@ -283,6 +303,7 @@ def forward_split(q, k, v, causal=False, scale=None, offset=None, window=0, nspl
         raise ValueError("q, k and v must share B and d")
     if any(x.dtype != torch.bfloat16 for x in (q, k, v)):
         raise ValueError("fa_fwd_split takes bfloat16 tensors")
+    _one_device(q, k, v)
     B, Hq, T, d = q.shape
     Hkv, S = k.shape[1], k.shape[2]
     q, k, v = (x.contiguous() for x in (q, k, v))
@@ -298,8 +319,9 @@ def forward_split(q, k, v, causal=False, scale=None, offset=None, window=0, nspl
         ws_o, ws_lse = workspace
         if (ws_o.dtype != torch.float32 or ws_lse.dtype != torch.float32 or not ws_o.is_contiguous()
                 or not ws_lse.is_contiguous() or ws_o.numel() < G * B * Hq * T * d
-                or ws_lse.numel() < G * B * Hq * T):
-            raise ValueError("workspace must be contiguous float32 tensors of G*B*Hq*T*d and G*B*Hq*T elements")
+                or ws_lse.numel() < G * B * Hq * T or ws_o.device != q.device or ws_lse.device != q.device):
+            raise ValueError("workspace must be contiguous float32 tensors on the device of q, of at least "
+                             "G*B*Hq*T*d and G*B*Hq*T elements")
     out = torch.empty_like(q)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):

@@ -217,3 +217,25 @@ def test_many_heads_short_rows(d, causal):
                                        1.0 / math.sqrt(d), causal)
         assert_close(f64(o[b:b + 1, h:h + 1]), f64(lse[b:b + 1, h:h + 1]), o_ref, lse_ref, torch.bfloat16,
                      f"b={b} h={h}")
+
+
+def test_binding_rejects_wrong_output_buffers():
+    """forward() checks caller-supplied O and LSE buffers (the C entry point
+    trusts the sizes it is given), and the split workspace."""
+    q = torch.zeros(1, 2, 40, 64, dtype=torch.bfloat16, device="cuda")
+    bad_out = [torch.empty(1, 2, 41, 64, dtype=torch.bfloat16, device="cuda"),      # shape
+               torch.empty(1, 2, 40, 64, dtype=torch.float32, device="cuda"),       # dtype
+               torch.empty(1, 2, 64, 40, dtype=torch.bfloat16, device="cuda").transpose(2, 3)]  # layout
+    for out in bad_out:
+        with pytest.raises(ValueError):
+            fa.forward(q, q, q, out=out)
+    for lse in (torch.empty(1, 2, 39, device="cuda"), torch.empty(1, 2, 40, dtype=torch.float64, device="cuda")):
+        with pytest.raises(ValueError):
+            fa.forward(q, q, q, lse=lse)
+    o, lse = fa.forward(q, q, q, out=torch.empty_like(q), lse=torch.empty(1, 2, 40, device="cuda"))
+    assert o.shape == q.shape and lse.shape == (1, 2, 40)
+    G = fa.fa_split_chunks(1000, 4)
+    k = torch.zeros(1, 2, 1000, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fa.forward_split(q[:, :, :1], k, k, causal=True, nsplit=4,
+                         workspace=(torch.empty(G * 2 * 64 - 1, device="cuda"), torch.empty(G * 2, device="cuda")))
