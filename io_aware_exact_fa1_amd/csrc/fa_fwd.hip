@@ -472,7 +472,10 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
                                    : lse[(size_t)bh * Nq + query];
         mine = x != x;
       }
-      if (lane == 0) wave_marked[w] = __builtin_amdgcn_ballot_w64(mine) != 0;
+      // (the ballot is taken by every lane, outside the lane-0 branch, so
+      // that it sees the whole wave)
+      const bool wave_mine = __builtin_amdgcn_ballot_w64(mine) != 0;
+      if (lane == 0) wave_marked[w] = wave_mine;
       __syncthreads();
       int any = 0;
 #pragma unroll
@@ -809,7 +812,8 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
   if (EXACT) return false;
   // any row of the unit marked? (the flags are rewritten only after this
   // barrier, by the recompute pass)
-  if (lane == 0) wave_marked[w] = __builtin_amdgcn_ballot_w64(unit_jumped) != 0;
+  const bool wave_jumped = __builtin_amdgcn_ballot_w64(unit_jumped) != 0;  // every lane votes
+  if (lane == 0) wave_marked[w] = wave_jumped;
   __syncthreads();
   int any = 0;
 #pragma unroll

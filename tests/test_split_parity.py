@@ -12,6 +12,7 @@ import torch
 from gpu_util import assert_close, f64, require_gpu, say
 from oracle.variants import attention_ex_ref, attention_ex_rows_ref, attention_split_ref, merge_partials_ref
 import io_aware_exact_fa1_amd as fa
+import workloads
 
 pytestmark = pytest.mark.gpu
 
@@ -131,6 +132,18 @@ def test_climbing_scores_take_the_exact_path():
     for d, T, S in ((128, 1, 4096), (64, 1, 4096), (128, 64, 2000)):
         q, k, v = _qkv(1, 4, 2, T, S, d, seed=d + T, ramp=300.0)
         _check(q, k, v, True, None, 0, 4, f"climbing d={d} T={T} S={S}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_score_jump_some_rows(d):
+    """Only a few scattered rows see their scores rise by 60 nats at key 800,
+    inside the second of three chunks: those rows' partials of that chunk
+    are marked and redone (large-tile split path, then the merge)."""
+    require_gpu()
+    rows = [(0, 100), (0, 131), (1, 257), (1, 299), (2, 200), (3, 163)]
+    q, k, v = workloads.make_jump_qkv(1, 4, 2, 300, 1500, d, rows, key0=800, seed=51 + d)
+    for off, w in ((1200, 0), (700, 500)):
+        _check(q, k, v, True, off, w, 3, f"jump rows d={d} offset={off} window={w}")
 
 
 def test_deterministic_and_workspace_reuse():

@@ -10,6 +10,7 @@ import torch
 from gpu_util import assert_close, f64, require_gpu, say
 from oracle.variants import attention_ex_ref, attention_ex_rows_ref
 import io_aware_exact_fa1_amd as fa
+import workloads
 
 pytestmark = pytest.mark.gpu
 
@@ -126,3 +127,45 @@ def test_long_context_gqa_window_sampled():
         ro, rl = attention_ex_rows_ref(f64(q[0, h]), f64(k[0, h // 8]), f64(v[0, h // 8]), 1 / np.sqrt(d), True,
                                        0, W, rows)
         assert_close(o[0, h, rows], lse[0, h, rows], ro, rl, torch.bfloat16, f"h={h}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_climbing_scores_take_the_exact_pass(d):
+    """Keys ramped along the mean query direction of each K/V group's first
+    head, so that the scores of many rows (of every head, scattered over
+    lanes and waves) climb by up to hundreds of nats: the rows that outgrow
+    the fixed reference of their first tile are redone by the exact pass,
+    with grouped heads, an offset and a window."""
+    require_gpu()
+    B, Hq, Hkv, T, S = 1, 4, 2, 300, 1500
+    g = torch.Generator(device="cpu")
+    g.manual_seed(77 + d)
+    q = torch.randn((B, Hq, T, d), generator=g)
+    k = torch.randn((B, Hkv, S, d), generator=g)
+    v = torch.randn((B, Hkv, S, d), generator=g)
+    qs = q[:, ::Hq // Hkv, :]                               # every row of the group's first head
+    u = qs.mean(dim=2, keepdim=True)
+    u = u / u.norm(dim=-1, keepdim=True)
+    per = 300.0 / (qs.norm(dim=-1).mean() / np.sqrt(d))
+    k = k + per * torch.linspace(0, 1, S)[None, None, :, None] * u
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    for off, w in ((S - T, 0), (700, 500), (S - T, 64)):
+        _check(q, k, v, True, off, w, f"climbing d={d} offset={off} window={w}")
+
+
+# (head, row) pairs whose scores jump at key 800: rows at lanes 4, 3, 1, 11,
+# 8 and 3 of their wave, one of them alone in head 3
+EX_JUMP_ROWS = [(0, 100), (0, 131), (1, 257), (1, 299), (2, 200), (3, 163)]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_score_jump_some_rows(d):
+    """Only the rows in EX_JUMP_ROWS see their scores rise by 60 nats at key
+    800 (past the reference of the first tile each of them sees), with
+    grouped heads, an offset and a window: those rows alone are marked and
+    redone."""
+    require_gpu()
+    B, Hq, Hkv, T, S = 1, 4, 2, 300, 1500
+    q, k, v = workloads.make_jump_qkv(B, Hq, Hkv, T, S, d, EX_JUMP_ROWS, key0=800, seed=41 + d)
+    for off, w in ((S - T, 0), (700, 500)):
+        _check(q, k, v, True, off, w, f"jump rows d={d} offset={off} window={w}")

@@ -18,7 +18,7 @@ from dataclasses import dataclass
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_qkv", "get", "hbm_once_bytes", "tile_stream_bytes"]
+__all__ = ["Workload", "WORKLOADS", "make_qkv", "make_jump_qkv", "get", "hbm_once_bytes", "tile_stream_bytes"]
 
 
 @dataclass(frozen=True)
@@ -92,6 +92,32 @@ def make_qkv(B, H, N, d, dtype=torch.bfloat16, seed=0, k_mult=1.0):
         k = k * float(k_mult)
     v = torch.randn(shape, generator=g, dtype=torch.float32)
     return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
+def make_jump_qkv(B, Hq, Hkv, T, S, d, rows, key0, lift=60.0, seed=0):
+    """Q [B, Hq, T, d], K and V [B, Hkv, S, d] (bf16, CPU) in which only the
+    chosen query rows see their scores jump.  Q, then K, then V are drawn
+    i.i.d. N(0, 1) in float32 from a CPU generator seeded with ``seed``, then
+    a unit vector u (a fourth draw, normalised) is projected out of every
+    query and key row; each (head, row) pair in ``rows`` gets
+    sqrt(lift * sqrt(d)) u added to its query, and every key from ``key0`` on
+    gets the same.  With the scale 1/sqrt(d) the chosen rows' scores rise by
+    ``lift`` nats at key ``key0``; the other rows hold no component along u
+    (up to the bf16 rounding)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn((B, Hq, T, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, S, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, S, d), generator=g, dtype=torch.float32)
+    u = torch.randn(d, generator=g, dtype=torch.float32)
+    u = u / u.norm()
+    q = q - (q @ u)[..., None] * u
+    k = k - (k @ u)[..., None] * u
+    a = math.sqrt(lift * math.sqrt(d))
+    for h, t in rows:
+        q[:, h, t] += a * u
+    k[:, :, key0:] += a * u
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
 def sample_rows(N, count, seed, include_ends=True):
