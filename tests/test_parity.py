@@ -184,7 +184,7 @@ def test_status_codes_through_binding():
 def test_score_jump_recompute(d, causal):
     """Scores that rise far above the first key tile's maximum (here by ~70
     in log2 units, past the fast kernel's fixed-reference slack) are redone
-    by the exact-rescaling kernel; the result must still match the oracle."""
+    by the exact recompute pass; the result must still match the oracle."""
     N = 700
     g = torch.Generator().manual_seed(d + causal)
     q = torch.ones(1, 2, N, d) + 0.1 * torch.randn(1, 2, N, d, generator=g)
