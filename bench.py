@@ -410,6 +410,7 @@ def main():
     w = workloads.get(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
 
     log(f"[bench] generating inputs {w.name} B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}")
     q, k, v = workloads.make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, w.k_mult)
@@ -507,6 +508,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
+        # per-launch kernel times (HIP events on the launch stream) and the device they ran on
+        "kernel_ms": {"avg": round(avg_ms, 4), "median": round(med_ms, 4), "min": round(launch_ms[0], 4)},
+        "device": {"arch": props.gcnArchName, "cus": props.multi_processor_count},
     }
     print(json.dumps(out), flush=True)
 

@@ -200,26 +200,31 @@ def test_score_jump_recompute(d, causal):
     assert_close(f64(o), f64(lse), o_ref, lse_ref, torch.bfloat16, f"jump d={d} causal={causal}")
 
 
-# (head, row) pairs whose scores jump: rows at lanes 11, 5, 11, 31, 0 and 27
-# of their wave, and head 1 with one marked row (lane 12 of wave 1, tile 1)
+# (head, row) pairs whose scores jump at key 150: rows at lanes 11, 5, 11,
+# 31, 0 and 27 of their wave, and head 1 with one marked row (lane 12 of
+# wave 1, tile 1)
 JUMP_ROWS = [(0, 203), (0, 261), (0, 299), (0, 511), (0, 640), (0, 699), (1, 300)]
+# jumps that start inside the last, ragged key tile (keys 695..699 of 700),
+# which also holds the causal diagonal of these rows
+TAIL_JUMP_ROWS = [(0, 697), (1, 699)]
 
 
+@pytest.mark.parametrize("rows,key0", [(JUMP_ROWS, 150), (TAIL_JUMP_ROWS, 695)], ids=["mid", "tail"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_score_jump_some_rows(d, causal):
-    """Only the rows in JUMP_ROWS see their scores rise by 60 nats at key
-    150, past the first key tile's reference: those rows alone are marked,
+def test_score_jump_some_rows(d, causal, rows, key0):
+    """Only the listed rows see their scores rise by 60 nats from key key0
+    on, past the first key tile's reference: those rows alone are marked,
     and each must be redone exactly however few of its tile's (or wave's)
     rows are marked with it."""
     N = 700
-    q, k, v = workloads.make_jump_qkv(1, 2, 2, N, N, d, JUMP_ROWS, key0=150, seed=31 + d)
+    q, k, v = workloads.make_jump_qkv(1, 2, 2, N, N, d, rows, key0=key0, seed=31 + d)
     scale = 1.0 / math.sqrt(d)
-    say("score jump, some rows", d, causal)
+    say("score jump, some rows", d, causal, key0)
     o, lse = run_gpu(q, k, v, causal, scale)
     o_ref, lse_ref = attention_ref(f64(q), f64(k), f64(v), scale, causal)
-    assert_close(f64(o), f64(lse), o_ref, lse_ref, torch.bfloat16, f"jump rows d={d} causal={causal}")
-    for h, t in JUMP_ROWS:  # the chosen rows did jump (their LSE is 60 nats up)
+    assert_close(f64(o), f64(lse), o_ref, lse_ref, torch.bfloat16, f"jump rows d={d} causal={causal} key0={key0}")
+    for h, t in rows:  # the chosen rows did jump (their LSE is ~60 nats up)
         assert lse_ref[0, h, t] > 50.0
 
 
