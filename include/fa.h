@@ -88,7 +88,12 @@ enum fa_status {
  * Arithmetic: Q K^T and P V run on bf16 matrix cores with fp32 accumulation;
  * the row max, the exponentials (base 2 with log2(e) folded into the scale),
  * the row sums, the running output and LSE are fp32; P is rounded to bf16
- * only as the operand of P V, while l sums the unrounded values.
+ * only as the operand of P V, while l sums the unrounded values.  The
+ * exponent reference of a row is the max of its first key tile (any common
+ * reference gives the same O and LSE); a row whose later weights outgrow it
+ * by more than 2^48 in a tile is redone, within the same launch, with the
+ * running-max rescaling on every tile.  LSE may transiently hold NaN for
+ * such a row while the launch runs; the returned values are final.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);
@@ -138,8 +143,8 @@ int fa_check_args(const void* q, const void* k, const void* v, const void* o, co
  *   B, d, scale, causal, stream: as for fa_fwd.
  * Errors as for fa_fwd, plus FA_ERR_VARIANT for Hq % Hkv != 0, S == 0, an
  * offset outside [0, S - T] or a window without the causal mask.  With
- * Hq == Hkv, T == S, offset 0 and no window the result equals fa_fwd's
- * (this entry point runs the same kernel with every tile masked).
+ * Hq == Hkv, T == S, offset 0 and no window the result equals fa_fwd's bit
+ * for bit (the same kernel, with the variants' index arithmetic).
  */
 int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int T,
               int S, int d, float scale, int causal, int offset, int window, hipStream_t stream);
