@@ -40,10 +40,10 @@ from .ref import as_f64, probabilities_ref
 
 
 def attention_bwd_ref(q, k, v, do, scale, causal):
-    """Gradients (dQ, dK, dV) of sum(O * dO) for one (batch, head) or a
-    batch of them ([..., N, d]), plus D (the row sums of P * dP), from the
-    plain definition: P is the materialised softmax of the scaled,
-    masked scores."""
+    """Gradients (dQ, dK, dV) of sum(O * dO) for one (batch, head): q, k, v
+    and do are [N, d]; plus D (the row sums of P * dP), from the plain
+    definition: P is the materialised softmax of the scaled, masked
+    scores."""
     q, k, v, do = (as_f64(x) for x in (q, k, v, do))
     p, _, _, _ = probabilities_ref(q, k, scale, causal)
     dv = np.swapaxes(p, -1, -2) @ do
