@@ -384,7 +384,8 @@ __device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
 // Arguments of the variants (EXT = true): query rows T and key rows S per
 // head, Hq query heads of which each group of `group` reads one K/V head,
 // the position of query row 0 (causal), a sliding window (0: none) and
-// whether work units pair a heavy and a light query tile.  Split-KV
+// whether work units pair a heavy and a light query tile (both launchers
+// set it; the plain kernel reads only this field).  Split-KV
 // (nsplit > 1): a work unit is (query tile, split); split g covers keys
 // [g * chunk, (g + 1) * chunk) and writes its normalised fp32 partial O_g
 // and LSE_g (-inf for a row with no visible key in the chunk) to
@@ -424,7 +425,7 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
   // EXT: T query rows and S key rows per head; otherwise both are N
   const int Nq = EXT ? ex.T : N;
   const int Nk = EXT ? ex.S : N;
-  if (CAUSAL && (!EXT || ex.pair)) {
+  if (CAUSAL && ex.pair) {
     tiles[0] = T_r - 1 - ur;  // heavy tile first
     tiles[1] = ur;
     ntiles = (tiles[1] < tiles[0]) ? 2 : 1;
@@ -872,17 +873,28 @@ int check(const void* q, const void* k, const void* v, const void* o, const floa
   return FA_OK;
 }
 
+// Causal work units pair the heavy query tile T_r-1-u with the light tile u,
+// so that every unit costs about the same -- when there are more query
+// tiles than compute units.  With fewer, every tile gets a compute unit of
+// its own: the call then takes as long as its heaviest tile, not as long as
+// the heaviest pair on half of the chip.
+constexpr long long kComputeUnits = 256;  // MI355X
+inline bool pair_tiles(long long heads, int T_r) { return heads * T_r > kComputeUnits; }
+
 template <class C, bool CAUSAL>
 void launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
                  float c, unsigned qsign, hipStream_t stream) {
   const int T_r = (N + C::BR - 1) / C::BR;
-  const int units_per_head = CAUSAL ? (T_r + 1) / 2 : T_r;
+  const int pair = CAUSAL && pair_tiles((long long)B * H, T_r);
+  const int units_per_head = pair ? (T_r + 1) / 2 : T_r;
   const int num_units = B * H * units_per_head;
   const int per_xcd = (num_units + 7) / 8;
   const int grid = per_xcd * 8;
+  ExtArgs ex{};
+  ex.pair = pair;
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<C, CAUSAL>), dim3(grid), dim3(C::NW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, N, T_r,
-                     units_per_head, num_units, per_xcd, c, qsign, ExtArgs{});
+                     units_per_head, num_units, per_xcd, c, qsign, ex);
 }
 
 template <class C, bool CAUSAL>
@@ -891,7 +903,7 @@ void launch_bf16_ex(const void* q, const void* k, const void* v, void* o, float*
                     int nsplit = 1, int chunk = 0, float* ws_o = nullptr, float* ws_lse = nullptr) {
   const int T_r = (T + C::BR - 1) / C::BR;
   // with a window (or split keys) every unit costs about the same: no pairing
-  const int pair = CAUSAL && window == 0 && nsplit == 1;
+  const int pair = CAUSAL && window == 0 && nsplit == 1 && pair_tiles((long long)B * Hq, T_r);
   const int units_per_head = pair ? (T_r + 1) / 2 : T_r * nsplit;
   const int num_units = B * Hq * units_per_head;
   const int per_xcd = (num_units + 7) / 8;
