@@ -198,7 +198,7 @@ __global__ void __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu
 fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                  const uint16_t* __restrict__ o, const float* __restrict__ lse, const uint16_t* __restrict__ dout,
                  uint16_t* __restrict__ dq, float* __restrict__ delta, int N, int T_r, int units_per_head,
-                 int num_units, int per_xcd, float c, float scale, unsigned ssign) {
+                 int num_units, int per_xcd, int pair, float c, float scale, unsigned ssign) {
   // a ring of DQ_NST stages of (K, V) tiles: copies run two tiles ahead
   __shared__ __attribute__((aligned(1024))) unsigned char smem[DQ_NST * C::DQSTAGE];
   const int lane = threadIdx.x & 63;
@@ -210,8 +210,9 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   if (u >= num_units) return;
   const int bh = u / units_per_head;
   const int ur = u - bh * units_per_head;
-  int tiles[2] = {CAUSAL ? T_r - 1 - ur : ur, ur};
-  const int ntiles = (CAUSAL && tiles[1] < tiles[0]) ? 2 : 1;
+  // causal pairs: the heavy query tile T_r-1-ur, then the light tile ur
+  int tiles[2] = {(CAUSAL && pair) ? T_r - 1 - ur : ur, ur};
+  const int ntiles = (CAUSAL && pair && tiles[1] < tiles[0]) ? 2 : 1;
 
   BLane<C> bl;
   blane<C>(bl, w, lane);
@@ -362,7 +363,7 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    const uint16_t* __restrict__ v, const float* __restrict__ lse,
                    const uint16_t* __restrict__ dout, const float* __restrict__ delta, uint16_t* __restrict__ dk,
                    uint16_t* __restrict__ dv, int N, int T_r, int units_per_head, int num_units, int per_xcd,
-                   float c, float scale, unsigned ssign) {
+                   int pair, float c, float scale, unsigned ssign) {
   // two stages of (Q, dO, L, D) tiles, then the V rows of the workgroup's keys
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE + C::ROWS * C::ROWB];
   const int lane = threadIdx.x & 63;
@@ -374,9 +375,9 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   if (u >= num_units) return;
   const int bh = u / units_per_head;
   const int ur = u - bh * units_per_head;
-  // causal: key tile 0 sees every query (heavy), the last tile the fewest
-  int tiles[2] = {ur, CAUSAL ? T_r - 1 - ur : ur};
-  const int ntiles = (CAUSAL && tiles[1] > tiles[0]) ? 2 : 1;
+  // causal pairs: key tile ur (it sees more queries), then T_r-1-ur
+  int tiles[2] = {ur, (CAUSAL && pair) ? T_r - 1 - ur : ur};
+  const int ntiles = (CAUSAL && pair && tiles[1] > tiles[0]) ? 2 : 1;
 
   BLane<C> bl;
   blane<C>(bl, w, lane);
@@ -586,18 +587,22 @@ void launch_bwd(const void* q, const void* k, const void* v, const void* o, cons
                 void* dq, void* dk, void* dv, float* delta, int B, int H, int N, float c, float scale,
                 unsigned ssign, hipStream_t stream) {
   const int T = (N + C::ROWS - 1) / C::ROWS;
-  const int units_per_head = CAUSAL ? (T + 1) / 2 : T;
+  // causal units pair a heavy tile with a light one when there are more
+  // tiles than the 256 CUs; with fewer, every tile gets a CU of its own (two
+  // unpaired heavy tiles sharing one CU were slower than their pairs)
+  const int pair = CAUSAL && (long long)B * H * T > 256;
+  const int units_per_head = pair ? (T + 1) / 2 : T;
   const int num_units = B * H * units_per_head;
   const int per_xcd = (num_units + 7) / 8;
   const int grid = per_xcd * 8;
   hipLaunchKernelGGL((fa_bwd_dq_kernel<C, CAUSAL>), dim3(grid), dim3(C::NW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, lse,
-                     (const uint16_t*)dout, (uint16_t*)dq, delta, N, T, units_per_head, num_units, per_xcd, c,
-                     scale, ssign);
+                     (const uint16_t*)dout, (uint16_t*)dq, delta, N, T, units_per_head, num_units, per_xcd, pair,
+                     c, scale, ssign);
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<C, CAUSAL>), dim3(grid), dim3(C::NW * 64), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, lse, (const uint16_t*)dout,
                      (const float*)delta, (uint16_t*)dk, (uint16_t*)dv, N, T, units_per_head, num_units, per_xcd,
-                     c, scale, ssign);
+                     pair, c, scale, ssign);
 }
 
 }  // namespace
