@@ -138,3 +138,102 @@ def test_random_backward(seed):
         emean = float(np.mean(np.abs(got - ref))) / s
         assert np.all(np.isfinite(got)), f"{what} {name}: non-finite"
         assert emax <= 1.6e-2 and emean <= 2e-3, f"{what} {name}: max {emax:.2e} mean {emean:.2e}"
+
+
+def _sampled_case(seed, bad):
+    """One larger random case, checked on sampled rows (the oracle computes
+    each sampled row on its own): fa_fwd, or fa_fwd_ex and fa_fwd_split, or
+    dQ of fa_bwd."""
+    from oracle import attention_bwd_rows_ref, attention_rows_ref
+    from oracle.variants import attention_ex_rows_ref
+
+    rng = np.random.default_rng(20000 + seed)
+    d = int(rng.choice([64, 128]))
+    scale = 1.0 / math.sqrt(d)
+
+    def check(o, l, ro, rl, what):
+        eo, el = np.abs(o - ro), np.abs(l - rl)
+        if not (np.isfinite(o).all() and np.isfinite(l).all() and eo.max() <= 2e-2 and eo.mean() <= 2e-3
+                and el.max() <= 1e-3):
+            bad.append(f"{what}: max|dO| {eo.max():.2e} mean {eo.mean():.2e} max|dLSE| {el.max():.2e}")
+
+    kind = seed % 3
+    if kind == 0:
+        B, H, N = int(rng.integers(1, 4)), int(rng.integers(1, 9)), int(rng.integers(1, 6000))
+        causal = bool(rng.integers(2))
+        if rng.integers(3) == 0:
+            rows = _jump_rows(rng, H, N, 6)
+            q, k, v = workloads.make_jump_qkv(B, H, H, N, N, d, rows, int(rng.integers(0, N)), seed=seed)
+        else:
+            q, k, v = workloads.make_qkv(B, H, N, d, torch.bfloat16, seed, float(rng.choice([1.0, 3.0])))
+        what = f"fwd seed={seed} B={B} H={H} N={N} d={d} causal={causal}"
+        say(what)
+        o, l = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        o, l = f64(o), f64(l)
+        rws = workloads.sample_rows(N, 48, seed)
+        for b in range(B):
+            h = int(rng.integers(H))
+            ro, rl = attention_rows_ref(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), scale, causal, rws)
+            check(o[b, h, rws], l[b, h, rws], ro, rl, f"{what} b={b} h={h}")
+    elif kind == 1:
+        B = int(rng.integers(1, 3))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+        S = int(rng.integers(1, 8000))
+        T = int(rng.integers(1, S + 1)) if rng.integers(2) else int(rng.integers(1, min(S, 16) + 1))
+        causal = bool(rng.integers(4))
+        off = int(rng.integers(0, S - T + 1)) if causal else 0
+        W = int(rng.integers(1, S + 1)) if causal and rng.integers(2) else 0
+        ns = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+        g = torch.Generator(device="cpu")
+        g.manual_seed(seed)
+        q = torch.randn((B, Hq, T, d), generator=g).to(torch.bfloat16)
+        k = torch.randn((B, Hkv, S, d), generator=g).to(torch.bfloat16)
+        v = torch.randn((B, Hkv, S, d), generator=g).to(torch.bfloat16)
+        what = f"variants seed={seed} B={B} Hq={Hq} Hkv={Hkv} T={T} S={S} d={d} causal={causal} off={off} W={W} ns={ns}"
+        say(what)
+        qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+        oe, le = fa.forward_ex(qd, kd, vd, causal=causal, offset=off, window=W)
+        os_, ls = fa.forward_split(qd, kd, vd, causal=causal, offset=off, window=W, nsplit=ns)
+        torch.cuda.synchronize()
+        rws = workloads.sample_rows(T, 32, seed)
+        grp = Hq // Hkv
+        for b in range(B):
+            h = int(rng.integers(Hq))
+            ro, rl = attention_ex_rows_ref(f64(q[b, h]), f64(k[b, h // grp]), f64(v[b, h // grp]), scale, causal,
+                                           off, W, rws)
+            check(f64(oe[b, h])[rws], f64(le[b, h])[rws], ro, rl, f"{what} fa_fwd_ex b={b} h={h}")
+            check(f64(os_[b, h])[rws], f64(ls[b, h])[rws], ro, rl, f"{what} fa_fwd_split b={b} h={h}")
+    else:
+        H, N = int(rng.integers(1, 5)), int(rng.integers(1, 3000))
+        causal = bool(rng.integers(2))
+        q, k, v = workloads.make_qkv(1, H, N, d, torch.bfloat16, seed)
+        g = torch.Generator(device="cpu")
+        g.manual_seed(seed + 1)
+        do = torch.randn((1, H, N, d), generator=g).to(torch.bfloat16)
+        what = f"bwd seed={seed} H={H} N={N} d={d} causal={causal}"
+        say(what)
+        qd, kd, vd, dod = (x.cuda() for x in (q, k, v, do))
+        o, l = fa.forward(qd, kd, vd, causal=causal, scale=scale)
+        dq, _, _, _ = fa.backward(qd, kd, vd, o, l, dod, causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        h = int(rng.integers(H))
+        rws = workloads.sample_rows(N, 24, seed)
+        ref = attention_bwd_rows_ref(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), f64(do[0, h]), scale, causal, rws)
+        got = f64(dq[0, h])[rws]
+        s = max(float(np.abs(ref).max()), 1.0)
+        e = np.abs(got - ref) / s
+        if not (np.isfinite(got).all() and e.max() <= 1.6e-2 and e.mean() <= 2e-3):
+            bad.append(f"{what} dQ: max {e.max():.2e} mean {e.mean():.2e}")
+
+
+def test_random_larger_sampled():
+    """120 larger random cases (N up to 6000 keys for fa_fwd, 8000 for the
+    variants and split counts up to 64, 3000 for the backward), each checked
+    on sampled rows against the oracle; every failure is listed."""
+    require_gpu()
+    bad = []
+    for seed in range(120):
+        _sampled_case(seed, bad)
+    assert not bad, "\n".join(bad)
