@@ -286,10 +286,10 @@ __device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& l
 // EXACT = false (fast kernel): the first tile (FIRST) sets the reference to
 // its row max; later tiles compute no max at all and return true in a lane
 // whose weights of this tile sum to more than 2^kSlack (which every weight
-// above 2^kSlack, or an overflow to +inf, implies).  MAXALL (the variants'
-// kernel): every tile computes its row max, and the reference is the max
-// of the first tile in which the row sees a key; MASK then also applies the
-// sliding window's lower bound when wnd > 0.
+// above 2^kSlack, or an overflow to +inf, implies).  MAXALL (masked tiles):
+// the tile computes its row max, and the reference is the max of the first
+// tile in which the row sees a key (later tiles keep it); MASK then also
+// applies the sliding window's lower bound when wnd > 0.
 // EXACT = true (recompute pass): m is the running max and l and acc are
 // rescaled by exp2(m_old - m_new) on every tile.
 template <class C, bool CAUSAL, bool MASK, bool EXACT, bool FIRST, bool MAXALL = false>
@@ -522,6 +522,25 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
       const int jh = max(1, gfirst - kt0);
       jhead = jh + ((1 - jh) & 3);  // the first j >= jh with j % 4 == 1 (unrolled stage order)
     }
+    // Causal pairs: the light tile, run second, walks its key tiles from the
+    // last to the first.  Every unit of a head then ends its light tile at
+    // the same step, so the units read each key tile together (once from
+    // HBM for all of them) instead of one after another from key 0 after
+    // the tiles have left the L2.  The masked tiles (the diagonal, a ragged
+    // end) then lead: tile j is key tile klast - j; the tiles from glast on,
+    // which some row does not see in full, come first, plus tile glast - 1,
+    // which every row sees, so that every row has set its reference (the
+    // max of its first tile with a visible key) before the unmasked tiles.
+    const bool desc = CAUSAL && ti == 1 && ex.pair;
+    const int klast = kt0 + nkv - 1;
+    if (desc) {
+      const int glast = min(Nk / C::BC, (qoff + q0 + 1) / C::BC);
+      const int jh = max(1, klast + 2 - glast);
+      jhead = jh + ((1 - jh) & 3);
+      nfull = nkv;
+    }
+    // key tile of step j (wave-uniform)
+    auto ktile = [&](int j) __attribute__((always_inline)) { return desc ? klast - j : kt0 + j; };
 
     float m = -INFINITY, lsum = 0.f;
     f32x16 acc[C::DB];
@@ -570,7 +589,7 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     auto mphase = [&](int j, int kst, int vst, int dst, auto has_qk, auto has_pv) __attribute__((always_inline)) {
       constexpr bool QK = decltype(has_qk)::value, PV = decltype(has_pv)::value;
       if (!VC) {
-        if (j + 2 < nkv) load_tile<C>(msrc, mdst + dst, (kt0 + j + 2) * C::BC, Nk, lo, w);
+        if (j + 2 < nkv) load_tile<C>(msrc, mdst + dst, ktile(j + 2) * C::BC, Nk, lo, w);
         if (QK) prefetch_k<C>(kpre, lo, kst);
       }
       tile_m<C, QK, PV>(kst, vst, lo, qr, s, p, acc, kpre);
@@ -590,12 +609,12 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     auto vphase = [&](int j, int dst, int kst1, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
       constexpr bool FIRST = decltype(first_tag)::value;
-      jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, EXT && MASK>(s, p, acc, m, lsum, (kt0 + j) * C::BC, qoff + qw0,
+      jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, MASK>(s, p, acc, m, lsum, ktile(j) * C::BC, qoff + qw0,
                                                                  Nk, c, lane, wnd);
       __builtin_amdgcn_sched_barrier(0);
       if (VC) {
         if (j + 3 < nkv) {
-          load_tile<C>(msrc, mdst + dst, (kt0 + j + 3) * C::BC, Nk, lo, w);
+          load_tile<C>(msrc, mdst + dst, ktile(j + 3) * C::BC, Nk, lo, w);
           wait_copies<C::NI>();
         } else {
           wait_copies<0>();
@@ -644,12 +663,12 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         constexpr bool LAG = decltype(lag_tag)::value;
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool FIRST = decltype(first_tag)::value;
-        jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, EXT && MASK>(s, p, acc, m, lsum, (kt0 + j) * C::BC,
+        jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, MASK>(s, p, acc, m, lsum, ktile(j) * C::BC,
                                                                    qoff + qw0, Nk, c, lane, wnd);
         __builtin_amdgcn_sched_barrier(0);
         const int ct = LAG ? j + 2 : j + 3;  // the tile this wave copies now
         if (ct < nkv) {
-          load_tile<C>(LAG ? vh : kh, lo.base + (LAG ? C::VBASE + s2 : s3), (kt0 + ct) * C::BC, Nk, lo, w);
+          load_tile<C>(LAG ? vh : kh, lo.base + (LAG ? C::VBASE + s2 : s3), ktile(ct) * C::BC, Nk, lo, w);
           wait_copies<C::NI>();
         } else {
           wait_copies<0>();
@@ -678,7 +697,7 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         };
         for (int t = 0; t < (LAG ? 2 : 3); ++t)
           if (t < nkv)
-            load_tile<C>(LAG ? vh : kh, lo.base + (LAG ? C::VBASE : 0) + stg(t), (kt0 + t) * C::BC, Nk, lo, w);
+            load_tile<C>(LAG ? vh : kh, lo.base + (LAG ? C::VBASE : 0) + stg(t), ktile(t) * C::BC, Nk, lo, w);
         wait_copies<0>();
         barrier();
         prefetch_k<C>(kpre, lo, 0);
@@ -732,7 +751,7 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     } else {
 
       for (int t = 0; t < AHEAD; ++t)
-        if (t < nkv) load_tile<C>(msrc, mdst + stg(t), (kt0 + t) * C::BC, Nk, lo, w);
+        if (t < nkv) load_tile<C>(msrc, mdst + stg(t), ktile(t) * C::BC, Nk, lo, w);
       wait_copies<0>();
       barrier();
       if (lag) barrier();
@@ -742,7 +761,7 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
       mphase(0, 0, 0, stg(AHEAD), std::true_type{}, std::false_type{});
       barrier();
       // (EXT: the first tile may be the window's left edge: always masked)
-      if (nfull > 0 && !EXT) vphase(0, stg(AHEAD), stg(1), std::false_type{}, std::true_type{});
+      if (nfull > 0 && !EXT && !desc) vphase(0, stg(AHEAD), stg(1), std::false_type{}, std::true_type{});
       else vphase(0, stg(AHEAD), stg(1), std::true_type{}, std::true_type{});
       // unmasked steps 1 .. j1-1, unrolled by the ring size so that every
       // stage offset is a compile-time constant (step j uses stage j % 4)
