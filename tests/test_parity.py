@@ -229,6 +229,24 @@ def test_score_jump_some_rows(d, causal, rows, key0):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_long_noncausal_rounds(d):
+    """N = 9000 without a mask: 36 query tiles per head, more than one XCD's
+    32 CUs run at once, and a ragged last key tile; sampled rows (including
+    the edges of the last tiles) of every fourth head, and every row
+    finite."""
+    require_gpu()
+    q, k, v = workloads.make_qkv(1, 8, 9000, d, torch.bfloat16, seed=900 + d)
+    say("long non-causal", d)
+    o, lse = run_gpu(q, k, v, False, 1.0 / math.sqrt(d))
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rows = workloads.sample_rows(9000, 96, seed=d)
+    rows = np.union1d(rows, np.array([8191, 8192, 8447, 8448, 8960, 8999]))  # tiles 31, 32, 33, 35
+    for h in range(0, 8, 4):
+        ro, rl = attention_rows_ref(f64(q[0, h]), f64(k[0, h]), f64(v[0, h]), 1.0 / math.sqrt(d), False, rows)
+        assert_close(f64(o[0, h])[rows], f64(lse[0, h])[rows], ro, rl, torch.bfloat16, f"long non-causal d={d} h={h}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_many_heads_short_rows(d, causal):
     """B = 16, H = 64, N = 65: 1024 heads of one full and one one-row query

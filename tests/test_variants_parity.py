@@ -169,3 +169,20 @@ def test_score_jump_some_rows(d):
     q, k, v = workloads.make_jump_qkv(B, Hq, Hkv, T, S, d, EX_JUMP_ROWS, key0=800, seed=41 + d)
     for off, w in ((S - T, 0), (700, 500)):
         _check(q, k, v, True, off, w, f"jump rows d={d} offset={off} window={w}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_cross_attention_rounds(d):
+    """T = 8500 queries over S = 3000 keys without a mask (34 query tiles per
+    head, more than one XCD runs at once), grouped heads; sampled rows
+    against the oracle."""
+    require_gpu()
+    q, k, v = _qkv(1, 4, 2, 8500, 3000, d, seed=950 + d)
+    say(f"long cross-attention d={d}")
+    o, lse = fa.forward_ex(q.cuda(), k.cuda(), v.cuda(), causal=False)
+    torch.cuda.synchronize()
+    rows = np.union1d(workloads.sample_rows(8500, 64, seed=d), np.array([8191, 8192, 8499]))
+    for h in (0, 3):
+        ro, rl = attention_ex_rows_ref(f64(q[0, h]), f64(k[0, h // 2]), f64(v[0, h // 2]), 1 / np.sqrt(d), False,
+                                       0, 0, rows)
+        assert_close(f64(o[0, h])[rows], f64(lse[0, h])[rows], ro, rl, torch.bfloat16, f"cross d={d} h={h}")
