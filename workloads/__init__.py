@@ -94,6 +94,20 @@ def make_qkv(B, H, N, d, dtype=torch.bfloat16, seed=0, k_mult=1.0):
     return q.to(dtype), k.to(dtype), v.to(dtype)
 
 
+def make_qkv_device(B, Hq, Hkv, T, S, d, dtype=torch.bfloat16, seed=0, device="cuda"):
+    """Q [B, Hq, T, d], K and V [B, Hkv, S, d] drawn i.i.d. N(0, 1) directly
+    in ``dtype`` on ``device`` by torch's generator for that device, seeded
+    with ``seed`` (Q, then K, then V).  For inputs of billions of elements,
+    which take too long to draw on the host; the tests copy the heads they
+    check back to the host for the oracle."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    q = torch.randn((B, Hq, T, d), generator=g, dtype=dtype, device=device)
+    k = torch.randn((B, Hkv, S, d), generator=g, dtype=dtype, device=device)
+    v = torch.randn((B, Hkv, S, d), generator=g, dtype=dtype, device=device)
+    return q, k, v
+
+
 def make_jump_qkv(B, Hq, Hkv, T, S, d, rows, key0, lift=60.0, seed=0):
     """Q [B, Hq, T, d], K and V [B, Hkv, S, d] (bf16, CPU) in which only the
     chosen query rows see their scores jump.  Q, then K, then V are drawn
