@@ -4,8 +4,9 @@ counts are drawn per case (the case's seed names it), and some cases plant
 scores that jump by 60 nats for a few random rows, so that the exact
 recompute pass runs on rows scattered over lanes, waves and query tiles.
 Tolerances are those of the dedicated parity tests: the bf16 and fp32
-forward bounds, and for the backward max |err| <= 1.6e-2 and mean |err| <=
-2e-3 relative to max(1, max |ref|)."""
+forward bounds (widened for the forward's sharper random scales where the
+rounding model gives more, see _forward_tol), and for the backward max
+|err| <= 1.6e-2 and mean |err| <= 2e-3 relative to max(1, max |ref|)."""
 
 import math
 
@@ -13,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import assert_close, f64, require_gpu, say
+from gpu_util import TOL, assert_close, f64, require_gpu, say
 from oracle import attention_bwd_ref, attention_ref
 from oracle.variants import attention_ex_ref
 import io_aware_exact_fa1_amd as fa
@@ -24,6 +25,24 @@ pytestmark = pytest.mark.gpu
 
 def _jump_rows(rng, Hq, T, n):
     return sorted({(int(rng.integers(Hq)), int(rng.integers(T))) for _ in range(n)})
+
+
+def _forward_tol(dtype, v, scale, d):
+    """The forward bounds, widened where the rounding model gives more than
+    they allow.  bf16: the weights P and the output O are each rounded to
+    bf16 (unit roundoff 2^-8), so |dO| <= 2^-8 max|V| + 2^-8 |O| <= 2^-7
+    max|V|; with sharp scales a row's O is close to one row of V and reaches
+    |V|'s tail (about 4.5 for these draws), past the 2e-2 that holds for
+    averaging rows.  fp32: the error of the logits, and with it that of O and
+    LSE, grows with |scale| sqrt(d), which is 1 at the usual scale."""
+    tol = dict(TOL[dtype])
+    if dtype == torch.bfloat16:
+        tol["o_max"] = max(tol["o_max"], 2.0 ** -7 * float(v.abs().max()) * 1.02)
+    else:
+        f = max(1.0, abs(scale) * math.sqrt(d))
+        tol["o_max"] *= f
+        tol["lse_max"] *= f
+    return tol
 
 
 @pytest.mark.parametrize("seed", range(24))
@@ -50,7 +69,7 @@ def test_random_forward(seed):
     o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
     torch.cuda.synchronize()
     ro, rl = attention_ref(f64(q), f64(k), f64(v), scale, causal)
-    assert_close(f64(o), f64(lse), ro, rl, dtype, what)
+    assert_close(f64(o), f64(lse), ro, rl, dtype, what, tol=_forward_tol(dtype, v, scale, d))
 
 
 def _variant_case(seed):
