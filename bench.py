@@ -56,7 +56,13 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X published dense bf16 matrix peak (2.5 PFLOP/s)
+# MI355X dense bf16 matrix peak: 256 compute units x 4096 bf16 FLOP per clock
+# per CU x 2.4 GHz peak engine clock = 2516.6 TFLOP/s (AMD's published
+# 2.5 PFLOP/s, unrounded); bf16_peak_tflops() uses the device's own CU count
+MI355X_CUS = 256
+BF16_FLOP_PER_CLK_PER_CU = 4096
+PEAK_SCLK_GHZ = 2.4
+PEAK_BF16_TFLOPS = MI355X_CUS * BF16_FLOP_PER_CLK_PER_CU * PEAK_SCLK_GHZ / 1e3
 DEFAULT_WORKLOAD = "longctx_n16384_d128_causal"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the sources that define the forward kernel (its counters are void once they change)
@@ -96,6 +102,24 @@ def parse():
                    help="run only a plain device copy of 1 GiB (5 times), to calibrate the HBM "
                         "byte counters (FETCH_SIZE / WRITE_SIZE) of a profiler run")
     return p.parse_args()
+
+
+def bf16_peak_tflops(cus=MI355X_CUS):
+    """Dense bf16 matrix peak of a device with ``cus`` compute units at the
+    peak engine clock."""
+    return cus * BF16_FLOP_PER_CLK_PER_CU * PEAK_SCLK_GHZ / 1e3
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def copy_calibration():
@@ -172,6 +196,7 @@ def cpu_baseline(w, q, k, v, target_s):
         "unit": "TFLOP/s",
         "cores": int(min(threads, cores)),
         "kind": "oracle",
+        "cpu": cpu_model(),
         "sample": (f"{heads} whole head(s) ({nrows} query rows) of {w.name}, each row computed on its own "
                    f"by the fp64 numpy oracle (attention_rows_ref), {el:.1f} s wall; "
                    f"{cores} host cores visible, BLAS threads {blas_threads}"),
@@ -213,6 +238,7 @@ def cpu_baseline_bwd(w, q, k, v, do, target_s):
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
+        "cpu": cpu_model(),
         "sample": (f"{nrows} query rows of {heads} head(s) of {w.name}: dQ of each row computed on its own by "
                    f"the fp64 numpy backward oracle (attention_bwd_rows_ref), {el:.1f} s wall; "
                    f"{cores} host cores visible"),
@@ -309,6 +335,55 @@ PEAK_FP32_TFLOPS = 157.3   # MI355X published fp32 vector peak (the fp32 config 
 PEAK_HBM_GBS = 8000.0      # MI355X published HBM3E bandwidth
 
 
+def cpu_oracle_full(w, q, k, v, workers):
+    """Time the fp64 oracle (``attention_ref`` as it stands) on the whole
+    workload: one (batch, head) per task on a pool of ``workers`` host
+    threads, BLAS held to one thread per task (numpy releases the GIL in
+    its matrix products and element-wise loops)."""
+    import concurrent.futures
+    import threadpoolctl
+    from oracle import attention_ref  # CPU baseline leg only
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def one(bh):
+        b, h = bh
+        attention_ref(q[b, h].double().numpy(), k[b, h].double().numpy(), v[b, h].double().numpy(),
+                      w.scale, w.causal)
+
+    with threadpoolctl.threadpool_limits(1, user_api="blas"):
+        t0 = time.perf_counter()
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, heads))
+        el = time.perf_counter() - t0
+    return {"value": w.flops / el / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": (f"the whole workload: {len(heads)} (batch, head) pairs of {w.name}, attention_ref "
+                       f"(fp64 numpy, S materialised) per pair on {workers} threads, {el:.1f} s wall")}
+
+
+def launch_floor(steps):
+    """Time per call of a graph-replayed one-element kernel: the floor under
+    any single-kernel call of a few microseconds."""
+    import torch
+    x = torch.zeros(1, device="cuda")
+    x.add_(1.0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            x.add_(1.0)
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def config_sweep(args):
     """One JSON line per workload: fa_fwd (fa_fwd_f32 for fp32) time from a
     HIP graph of `steps` calls and from eager calls, TFLOP/s against the
@@ -321,8 +396,14 @@ def config_sweep(args):
 
     fa.load_library()
     dev = torch.device("cuda:0")
+    floor = launch_floor(args.steps)
+    print(json.dumps({"workload": "launch_floor", "note": "graph-replayed one-element torch kernel (x.add_)",
+                      "ms": round(floor, 5)}), flush=True)
+    peak_bf16 = round(bf16_peak_tflops(torch.cuda.get_device_properties(dev).multi_processor_count), 1)
+    workers = min(16, len(os.sched_getaffinity(0)))
     for name, w in workloads.WORKLOADS.items():
-        q, k, v = (x.to(dev) for x in workloads.make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, w.k_mult))
+        qc, kc, vc = workloads.make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, w.k_mult)
+        q, k, v = (x.to(dev) for x in (qc, kc, vc))
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
         variants = [("fa_fwd_f32" if w.dtype == "f32" else "fa_fwd", 1)]
@@ -369,15 +450,20 @@ def config_sweep(args):
             e1.record(stream)
             torch.cuda.synchronize()
             ms_eager = e0.elapsed_time(e1) / args.steps
-            peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+            peak = PEAK_FP32_TFLOPS if w.dtype == "f32" else peak_bf16
             tf = w.flops / ms / 1e9
             gbs = w.algorithmic_bytes / ms / 1e6
-            print(json.dumps({"workload": name, "note": w.note, "entry": entry, "nsplit": nsplit, "chunks": G,
-                              "ms": round(ms, 5), "ms_eager": round(ms_eager, 5),
-                              "tflops": round(tf, 2), "peak_tflops": peak, "frac_peak": round(tf / peak, 4),
-                              "algorithmic_bytes": w.algorithmic_bytes, "gbs": round(gbs, 1),
-                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "graph_equals_eager": same}), flush=True)
+            line = {"workload": name, "note": w.note, "entry": entry, "nsplit": nsplit, "chunks": G,
+                    "ms": round(ms, 5), "ms_eager": round(ms_eager, 5),
+                    "tflops": round(tf, 2), "peak_tflops": peak, "frac_peak": round(tf / peak, 4),
+                    "algorithmic_bytes": w.algorithmic_bytes, "gbs": round(gbs, 1),
+                    "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "graph_equals_eager": same}
             del graph, ws
+            if nsplit == 1 and not args.no_cpu_baseline and name != DEFAULT_WORKLOAD:
+                # (the long-context workload's oracle time is the main bench's cpu_baseline leg)
+                log(f"[configs] timing the CPU oracle on the whole of {name}")
+                line["cpu_baseline"] = cpu_oracle_full(w, qc, kc, vc, workers)
+            print(json.dumps(line), flush=True)
         del q, k, v, o, lse
 
 
@@ -471,9 +557,10 @@ def main():
     tflop = flops / 1e12
     value = tflop / (ms_per_step / 1e3)
     achieved = tflop / (avg_ms / 1e3)
+    peak = round(bf16_peak_tflops(props.multi_processor_count), 1)
     log(f"[bench] {w.name}: wall {ms_per_step:.3f} ms/step, kernel avg {avg_ms:.3f} ms "
         f"(median {med_ms:.3f}, min {launch_ms[0]:.3f}) -> {achieved:.1f} TFLOP/s "
-        f"= {100 * achieved / PEAK_BF16_TFLOPS:.1f}% of bf16 dense peak")
+        f"= {100 * achieved / peak:.1f}% of the {peak} TFLOP/s bf16 dense peak")
 
     traffic = None if args.backward else measured_traffic(w.name)
 
@@ -504,9 +591,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
                    "scale": w.scale, "pass": "backward" if args.backward else "forward",
-                   "flops_per_step": flops, "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+                   "flops_per_step": flops, "pct_of_bf16_peak": round(100 * value / peak, 2)},
+        # peak = CUs x 4096 bf16 FLOP/clk/CU x 2.4 GHz (the published 2.5 PFLOP/s, unrounded)
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         # per-launch kernel times (HIP events on the launch stream) and the device they ran on
         "kernel_ms": {"avg": round(avg_ms, 4), "median": round(med_ms, 4), "min": round(launch_ms[0], 4)},

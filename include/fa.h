@@ -90,10 +90,15 @@ enum fa_status {
  * the row sums, the running output and LSE are fp32; P is rounded to bf16
  * only as the operand of P V, while l sums the unrounded values.  The
  * exponent reference of a row is the max of its first key tile (any common
- * reference gives the same O and LSE); a row whose later weights outgrow it
- * by more than 2^48 in a tile is redone, within the same launch, with the
- * running-max rescaling on every tile.  LSE may transiently hold NaN for
- * such a row while the launch runs; the returned values are final.
+ * reference gives the same O and LSE in exact arithmetic); on a tile where
+ * a row's weights would outgrow it by more than 2^16, that row takes the
+ * running-max step of the recurrence ("15. FlashAttention", section "Online
+ * softmax: normalize as you go": new reference, l and the accumulator
+ * rescaled by exp(m_old - m_new)), so no weight exceeds 2^16.
+ * Range: the fp32 accumulator then holds at most N * 2^16 * max|V|, so the
+ * results are those of the recurrence while N * max|V| stays below about
+ * 2^112 (the recurrence's own fp32 accumulator needs N * max|V| below
+ * about 2^128); beyond that, O may overflow to inf.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, hipStream_t stream);

@@ -38,10 +38,11 @@
 //    cores while the other computes exponentials.  In the matrix phase
 //    every LDS address is a per-lane offset computed once plus an
 //    immediate, so that phase issues no vector-ALU work at all.
-//  * The exponent reference of a row is fixed after its first key tile
-//    (no rescaling of acc in the loop); rows whose scores later jump too
-//    far above it are redone, by the same workgroup right after its fast
-//    pass, with exact rescaling (one launch per call).
+//  * The exponent reference of a row is fixed after its first key tile, so
+//    the loop normally rescales nothing; a wave whose weights outgrow it by
+//    more than 2^16 in a tile takes the running-max step of the recurrence
+//    for that tile (new reference, acc and l rescaled, weights formed
+//    again), so the weights stay bounded.
 //  * Exponentials are exp2 with log2(e) folded into the scale; m, l and the
 //    output accumulator stay in fp32 registers; O is divided by l once.
 //  * Work units are query tiles (causal: a heavy tile paired with a light
@@ -68,18 +69,21 @@ namespace {
 
 using namespace fa;
 
-// Exponent reference of the fast kernel.  Each row's reference m is fixed
-// at the max of its first key tile, and later tiles compute no max.  While
-// the weights p = exp2(s*c - m) that one lane sums per tile stay <= 2^kSlack
-// (so every single weight does), l <= N * 2^kSlack < 2^79 and acc cannot
-// overflow for |V| < 2^49; since O = acc / l and LSE = m + log2 l use one
-// common m, the result equals the running-max recurrence in exact
-// arithmetic (the recurrence holds for any common reference; the running
-// max only bounds the exponents).  A row whose tile sum exceeds the bound
-// (a score jumped more than kSlack above the reference, or overflowed to
-// +inf) is marked (NaN LSE) and recomputed by the exact-rescaling pass.
-constexpr float kSlack = 48.0f;
-constexpr float kJumpSum = 0x1p48f;  // 2^kSlack
+// Exponent reference.  A row's reference m is the max of its first key
+// tile with a visible key, and later unmasked tiles compute no max: their
+// weights are p = exp2(s*c - m) against that fixed m.  O = acc / l and
+// LSE = m + log2 l are the same for any common reference in exact
+// arithmetic (the running max of the recurrence only bounds the exponents),
+// so this equals the pages' recurrence as long as the weights stay bounded.
+// They are kept <= 2^kSlack: when the weights one lane sums for a tile
+// exceed 2^kSlack (a score rose more than kSlack above the reference, or an
+// exponential overflowed), or a masked tile's max rises more than kSlack
+// above it, the wave takes the recurrence's step for that tile -- the new
+// reference is the running max, l and acc are multiplied by
+// exp2(m_old - m_new), and the tile's weights are formed again.  Then
+// l <= N * 2^kSlack and |acc| <= N * 2^kSlack * max|V|.
+constexpr float kSlack = 16.0f;
+constexpr float kJumpSum = 0x1p16f;  // 2^kSlack
 
 // ---------------------------------------------------------------------------
 // Tile configuration of the bf16 kernel: 8 waves of 32 query rows each
@@ -279,30 +283,81 @@ __device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& l
   }
 }
 
+// Row max of the score tile in fp32, both halves of the wave (four
+// independent max chains over this half's keys, then one lane swap).
+template <class C>
+__device__ __forceinline__ float tile_rowmax(const f32x16 (&s)[C::SB]) {
+  float mq[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) mq[r] = s[0][r];
+#pragma unroll
+  for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+    for (int i = (sb == 0 ? 4 : 0); i < 16; ++i) mq[i & 3] = __builtin_fmaxf(mq[i & 3], s[sb][i]);
+  return half_max(__builtin_fmaxf(__builtin_fmaxf(mq[0], mq[1]), __builtin_fmaxf(mq[2], mq[3])));
+}
+
+// The recurrence's step ("15. FlashAttention", section "Online softmax:
+// normalize as you go") for the rows with `up` set: the reference moves up
+// to the running max m_new = max(m, mxs), and l and acc are multiplied by
+// exp2(m - m_new).  Other rows keep every bit as it is, so that a row's
+// result never depends on what other rows of its wave see.
+template <class C>
+__device__ __forceinline__ void raise_ref(bool up, float mxs, float& m, float& lsum, f32x16 (&acc)[C::DB]) {
+  const float m_new = up ? __builtin_fmaxf(m, mxs) : m;
+  const float alpha = m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+  lsum *= alpha;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+  m = m_new;
+}
+
+// P = exp2(S*c - mref) in place (masked scores give exp2(-inf) = 0); returns
+// this lane's sum of the unrounded weights.
+template <class C>
+__device__ __forceinline__ float tile_exp(f32x16 (&s)[C::SB], float c, float mref) {
+  float sq[4];
+#pragma unroll
+  for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[sb][i] = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c, -mref));
+      if (sb == 0 && i < 4) sq[i] = s[sb][i];
+      else sq[i & 3] += s[sb][i];
+    }
+  return (sq[0] + sq[1]) + (sq[2] + sq[3]);
+}
+
 // The vector-ALU phase: online softmax of one tile.  Mask (MASK: keys past
-// N, and keys after the query when causal, get -inf, i.e. weight exactly
-// 0), exponent reference, P = exp2(S*c - m_ref) into the bf16 operand pb,
-// row sum of the unrounded weights into lsum.
-// EXACT = false (fast kernel): the first tile (FIRST) sets the reference to
-// its row max; later tiles compute no max at all and return true in a lane
-// whose weights of this tile sum to more than 2^kSlack (which every weight
-// above 2^kSlack, or an overflow to +inf, implies).  MAXALL (masked tiles):
-// the tile computes its row max, and the reference is the max of the first
-// tile in which the row sees a key (later tiles keep it); MASK then also
-// applies the sliding window's lower bound when wnd > 0.
-// EXACT = true (recompute pass): m is the running max and l and acc are
-// rescaled by exp2(m_old - m_new) on every tile.
-template <class C, bool CAUSAL, bool MASK, bool EXACT, bool FIRST, bool MAXALL = false>
-__device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB],
+// N, and keys after the query when causal, get -inf, i.e. weight exactly 0;
+// with a sliding window (wnd > 0) also keys before query - wnd + 1),
+// exponent reference, P = exp2(S*c - m_ref) into the bf16 operand pb, row
+// sum of the unrounded weights into lsum.
+//  * FIRST / MASK tiles compute their row max.  The reference is the max of
+//    the row's first tile with a visible key (a row that has seen none yet
+//    uses the safe reference 0); a row whose max in a masked tile rises more
+//    than kSlack above it raises it (raise_ref, behind a wave-uniform
+//    branch).
+//  * Other tiles compute no max.  When the weights of either half of a row
+//    sum to more than 2^kSlack (every weight above 2^kSlack, or an overflow
+//    to +inf, implies that), the wave forms the tile's scores again
+//    (rescore: S = K Q^T from the K tile still in LDS, the same bits), those
+//    rows raise their reference to the running max, and every row forms its
+//    weights again (unchanged bits for the other rows: same scores, same
+//    reference).
+template <class C, bool CAUSAL, bool MASK, bool FIRST, class Rescore>
+__device__ __forceinline__ void tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB],
                                              float& m, float& lsum, int k0, int qw0, int N, float c, int lane,
-                                             int wnd = 0) {
+                                             int wnd, Rescore&& rescore) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
   // register i of block sb holds key k0 + 32*sb + 8*(i/4) + 4h + i%4
   if (MASK) {
     const int query = qw0 + l32;  // the query's position
     const int lim = (CAUSAL ? min(query, N - 1) : N - 1) - (k0 + 4 * h);
-    if (MAXALL && wnd > 0) {
+    if (wnd > 0) {
       // sliding window: keys query - wnd + 1 .. query
       const int low = query - wnd + 1 - (k0 + 4 * h);
 #pragma unroll
@@ -320,51 +375,29 @@ __device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
           s[sb][i] = (32 * sb + 8 * (i >> 2) + (i & 3) <= lim) ? s[sb][i] : -INFINITY;
     }
   }
-  bool had_ref = true;  // the fixed reference was set before this tile
-  if (EXACT || FIRST || MAXALL) {
-    // row max: four independent max chains over this half's keys, then the
-    // two halves of the wave
-    float mq[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mq[r] = s[0][r];
-#pragma unroll
-    for (int sb = 0; sb < C::SB; ++sb)
-#pragma unroll
-      for (int i = (sb == 0 ? 4 : 0); i < 16; ++i) mq[i & 3] = __builtin_fmaxf(mq[i & 3], s[sb][i]);
-    const float mx = half_max(__builtin_fmaxf(__builtin_fmaxf(mq[0], mq[1]), __builtin_fmaxf(mq[2], mq[3])));
+  if (FIRST || MASK) {
+    const float mx = tile_rowmax<C>(s);
     const float mxs = (mx == -INFINITY) ? -INFINITY : mx * c;  // c > 0
-    if (EXACT) {
-      const float m_new = __builtin_fmaxf(m, mxs);
-      const float mref_new = (m_new == -INFINITY) ? 0.f : m_new;  // safe reference
-      const float alpha = __builtin_amdgcn_exp2f(m - mref_new);    // 0 when m = -inf
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      m = m_new;
-    } else {
-      // the reference is the max of the first tile with a visible key
-      had_ref = m != -INFINITY;
-      m = had_ref ? m : mxs;
+    const bool had_ref = m != -INFINITY;
+    const bool up = had_ref && mxs > m + kSlack;  // (the same in both halves of a row)
+    if (!FIRST && __builtin_amdgcn_ballot_w64(up) != 0) raise_ref<C>(up, mxs, m, lsum, acc);
+    // the reference is the max of the first tile with a visible key
+    m = had_ref ? m : mxs;
+  }
+  // safe reference (a row with no visible key yet: 0); after its first
+  // tile with a visible key, m is finite
+  const float mref = (FIRST || MASK) ? ((m == -INFINITY) ? 0.f : m) : m;
+  float ts = tile_exp<C>(s, c, mref);
+  if (!FIRST && !MASK) {
+    // (NaN-safe: a NaN sum, from NaN inputs, does not take the branch)
+    if (__builtin_amdgcn_ballot_w64(ts > kJumpSum) != 0) {
+      const bool up = half_max(ts) > kJumpSum;  // either half of the row
+      rescore();
+      const float mx = tile_rowmax<C>(s);
+      raise_ref<C>(up, mx * c, m, lsum, acc);
+      ts = tile_exp<C>(s, c, m);
     }
   }
-  // safe reference; after the first tile of the fast kernel m is the finite
-  // max of a tile that holds a visible key of every row (key 0), except
-  // with a window (MAXALL), where a row may see its first key later
-  const float mref = (EXACT || FIRST || MAXALL) ? ((m == -INFINITY) ? 0.f : m) : m;
-
-  // P = exp2(S*c - m_ref); masked scores give exp2(-inf) = 0
-  float sq[4];
-#pragma unroll
-  for (int sb = 0; sb < C::SB; ++sb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[sb][i] = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c, -mref));
-      if (sb == 0 && i < 4) sq[i] = s[sb][i];
-      else sq[i & 3] += s[sb][i];
-    }
-  const float ts = (sq[0] + sq[1]) + (sq[2] + sq[3]);
   lsum += ts;
 #pragma unroll
   for (int kb2 = 0; kb2 < C::PB; ++kb2) {
@@ -373,12 +406,6 @@ __device__ __forceinline__ bool tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
     pin(pb[kb2]);
   }
   pin(lsum);
-  if (EXACT) {
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) pin(acc[db]);
-  }
-  // NaN-safe: a NaN sum (NaN inputs) is not flagged
-  return !EXACT && !FIRST && had_ref && ts > kJumpSum;
 }
 
 // Arguments of the variants (EXT = true): query rows T and key rows S per
@@ -397,18 +424,13 @@ struct ExtArgs {
   float* ws_lse;
 };
 
-// One work unit.  EXACT = false: the fast pass over the unit's query
-// tiles; returns (workgroup-uniform) whether it marked a row (NaN LSE).
-// EXACT = true: the recompute pass, which only redoes the query rows marked
-// (NaN LSE) and skips tiles without a marked row.  smem: the K/V ring, then
-// one flag per wave.
-template <class C, bool CAUSAL, bool EXACT, bool EXT>
-__device__ __attribute__((always_inline)) inline bool
+// One work unit: its query tiles, each over its key tiles.  smem: the K/V
+// ring.
+template <class C, bool CAUSAL, bool EXT>
+__device__ __attribute__((always_inline)) inline void
 fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
          uint16_t* __restrict__ o, float* __restrict__ lse, int N, int T_r, int units_per_head, int num_units,
          int per_xcd, float c, unsigned int qsign, const ExtArgs& ex, unsigned char LDS_AS* smem) {
-  int LDS_AS* wave_marked = (int LDS_AS*)(smem + C::LDSB);
-
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int l32 = lane & 31;
@@ -417,7 +439,7 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
   // Workgroups are dispatched round-robin over the 8 XCDs: block b runs on
   // XCD b % 8.  Give XCD x the contiguous units [x*per_xcd, (x+1)*per_xcd).
   const int u = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (u >= num_units) return false;
+  if (u >= num_units) return;
   const int bh = u / units_per_head;
   const int ur = u - bh * units_per_head;
   int tiles[2];
@@ -458,32 +480,11 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
   const int qoff = (EXT && CAUSAL) ? ex.offset : 0;   // position of query row 0
   const int wnd = (EXT && CAUSAL) ? ex.window : 0;    // sliding window (0: none)
 
-  bool unit_jumped = false;  // fast pass: a row of this wave was marked
   for (int ti = 0; ti < ntiles; ++ti) {
     // (EXT: said to be wave-uniform, so that the addresses derived from it
     // stay scalar)
     const int q0 = EXT ? __builtin_amdgcn_readfirstlane(tiles[ti] * C::BR) : tiles[ti] * C::BR;
     const int qw0 = q0 + w * 32;
-
-    bool mine = false;  // recompute pass: this lane's row was marked
-    if (EXACT) {
-      const int query = qw0 + l32;
-      if (query < Nq) {
-        const float x = split_mode ? ex.ws_lse[((size_t)split * ex.BH + bh) * Nq + query]
-                                   : lse[(size_t)bh * Nq + query];
-        mine = x != x;
-      }
-      // (the ballot is taken by every lane, outside the lane-0 branch, so
-      // that it sees the whole wave)
-      const bool wave_mine = __builtin_amdgcn_ballot_w64(mine) != 0;
-      if (lane == 0) wave_marked[w] = wave_mine;
-      __syncthreads();
-      int any = 0;
-#pragma unroll
-      for (int ww = 0; ww < C::NW; ++ww) any |= wave_marked[ww];
-      __syncthreads();  // wave_marked is rewritten for the next tile
-      if (!__builtin_amdgcn_readfirstlane(any)) continue;
-    }
 
     // Q_i rows as the B operand of S^T = K Q^T: lane holds query qw0 + l%32,
     // dims 16*kb + 8*(l/32) .. +7.  Rows past N are clamped (never stored).
@@ -548,8 +549,6 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-    bool jumped = false;
-
     // (split-KV: a chunk beyond every row's last visible key has no tiles)
     if (!EXT || nkv > 0) {
     // Phases.  Each step j of a wave is a matrix-core phase M(j) -- S_j =
@@ -584,6 +583,17 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     f32x16 s[C::SB];
     bf16x8 p[C::PB];  // P_{j-1} is read in M(j), then P_j is written in V(j)
     bf16x8 kpre[C::KD][C::SB];
+    // S_j = K_j Q^T once more, from the K tile at stage offset kst (still in
+    // LDS during the vector phase of step j): the rare path of tile_softmax
+    auto rescore_at = [&](int kst) __attribute__((always_inline)) {
+      const f32x16 zero = {};
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb)
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_k<C>(lo, kst, kb, sb), qr[kb], kb == 0 ? zero : s[sb],
+                                                          0, 0, 0);
+    };
     // M(j) (HAS_QK: K_j at stage offset kst; HAS_PV: V_{j-1} at vst); !VCOPY:
     // copies for tile j+2 into stage offset dst
     auto mphase = [&](int j, int kst, int vst, int dst, auto has_qk, auto has_pv) __attribute__((always_inline)) {
@@ -606,11 +616,11 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     };
     // V(j): softmax of tile j; VCOPY: copies for tile j+3 into stage offset
     // dst, then read ahead K of tile j+1 at stage offset kst1
-    auto vphase = [&](int j, int dst, int kst1, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
+    auto vphase = [&](int j, int kst0, int dst, int kst1, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
       constexpr bool FIRST = decltype(first_tag)::value;
-      jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, MASK>(s, p, acc, m, lsum, ktile(j) * C::BC, qoff + qw0,
-                                                                 Nk, c, lane, wnd);
+      tile_softmax<C, CAUSAL, MASK, FIRST>(s, p, acc, m, lsum, ktile(j) * C::BC, qoff + qw0, Nk, c, lane, wnd,
+                                           [&]() __attribute__((always_inline)) { rescore_at(kst0); });
       __builtin_amdgcn_sched_barrier(0);
       if (VC) {
         if (j + 3 < nkv) {
@@ -630,7 +640,7 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     auto step = [&](int j, int kst, int vst, int dst, int kst1, auto mask_tag) __attribute__((always_inline)) {
       mphase(j, kst, vst, dst, std::true_type{}, std::true_type{});
       barrier();
-      vphase(j, dst, kst1, mask_tag, std::false_type{});
+      vphase(j, kst, dst, kst1, mask_tag, std::false_type{});
     };
     constexpr int KT = C::KT;
     auto stg = [](int t) __attribute__((always_inline)) { return (t & 3) * KT; };
@@ -657,14 +667,14 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
       };
-      // V(j) with the stages of tiles j+1, j+2, j+3 (LAG: this wave is in the
-      // lagging half, which copies V; the leading half copies K)
-      auto v1 = [&](int j, int s1, int s2, int s3, auto lag_tag, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
+      // V(j) with the stages of tiles j, j+1, j+2, j+3 (LAG: this wave is in
+      // the lagging half, which copies V; the leading half copies K)
+      auto v1 = [&](int j, int s0, int s1, int s2, int s3, auto lag_tag, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
         constexpr bool LAG = decltype(lag_tag)::value;
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool FIRST = decltype(first_tag)::value;
-        jumped |= tile_softmax<C, CAUSAL, MASK, EXACT, FIRST, MASK>(s, p, acc, m, lsum, ktile(j) * C::BC,
-                                                                   qoff + qw0, Nk, c, lane, wnd);
+        tile_softmax<C, CAUSAL, MASK, FIRST>(s, p, acc, m, lsum, ktile(j) * C::BC, qoff + qw0, Nk, c, lane, wnd,
+                                             [&]() __attribute__((always_inline)) { rescore_at(s0); });
         __builtin_amdgcn_sched_barrier(0);
         const int ct = LAG ? j + 2 : j + 3;  // the tile this wave copies now
         if (ct < nkv) {
@@ -687,11 +697,11 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         // window j for 1 <= j < nkv - 1, stages of tiles j-1 .. j+3
         auto window = [&](int j, int sm1, int s0, int s1, int s2, int s3, auto mask_tag) __attribute__((always_inline)) {
           if (!LAG) {
-            v1(j, s1, s2, s3, lag_tag, mask_tag, F);
+            v1(j, s0, s1, s2, s3, lag_tag, mask_tag, F);
             m1(s1, s0, T, T);
           } else {
             m1(s0, sm1, T, T);
-            v1(j, s1, s2, s3, lag_tag, mask_tag, F);
+            v1(j, s0, s1, s2, s3, lag_tag, mask_tag, F);
           }
           barrier();
         };
@@ -706,12 +716,12 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         barrier();
         // window 0 (its tile may need the mask: the mask is exact on any tile)
         if (!LAG) {
-          v1(0, stg(1), stg(2), stg(3), lag_tag, T, T);
+          v1(0, stg(0), stg(1), stg(2), stg(3), lag_tag, T, T);
           if (1 < nkv) m1(stg(1), stg(0), T, T);
           else m1(0, stg(0), F, T);
         } else {
           m1(0, 0, T, F);
-          v1(0, stg(1), stg(2), stg(3), lag_tag, T, T);
+          v1(0, stg(0), stg(1), stg(2), stg(3), lag_tag, T, T);
         }
         barrier();
         // unmasked windows 1 .. j1-1, unrolled by the ring size so that
@@ -734,11 +744,11 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         if (nkv >= 2) {
           const int jl = nkv - 1;
           if (!LAG) {
-            v1(jl, stg(jl + 1), stg(jl + 2), stg(jl + 3), lag_tag, T, F);
+            v1(jl, stg(jl), stg(jl + 1), stg(jl + 2), stg(jl + 3), lag_tag, T, F);
             m1(0, stg(jl), F, T);
           } else {
             m1(stg(jl), stg(jl - 1), T, T);
-            v1(jl, stg(jl + 1), stg(jl + 2), stg(jl + 3), lag_tag, T, F);
+            v1(jl, stg(jl), stg(jl + 1), stg(jl + 2), stg(jl + 3), lag_tag, T, F);
           }
           barrier();
         }
@@ -761,8 +771,8 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
       mphase(0, 0, 0, stg(AHEAD), std::true_type{}, std::false_type{});
       barrier();
       // (EXT: the first tile may be the window's left edge: always masked)
-      if (nfull > 0 && !EXT && !desc) vphase(0, stg(AHEAD), stg(1), std::false_type{}, std::true_type{});
-      else vphase(0, stg(AHEAD), stg(1), std::true_type{}, std::true_type{});
+      if (nfull > 0 && !EXT && !desc) vphase(0, 0, stg(AHEAD), stg(1), std::false_type{}, std::true_type{});
+      else vphase(0, 0, stg(AHEAD), stg(1), std::true_type{}, std::true_type{});
       // unmasked steps 1 .. j1-1, unrolled by the ring size so that every
       // stage offset is a compile-time constant (step j uses stage j % 4)
       const int j1 = max(1, min(nfull, nkv));
@@ -790,14 +800,11 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
 
     // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
     const float lt = half_sum(lsum);
-    // a row is marked when either half of its keys flagged a jump
-    jumped = half_max(jumped ? 1.f : 0.f) != 0.f;
-    unit_jumped |= jumped;
     // (split-KV: no visible key in this chunk -> O_g = 0, LSE_g = -inf)
     const bool empty = EXT && !(lt > 0.f);
     const float inv = empty ? 0.f : 1.f / lt;
     const int query = qw0 + l32;
-    if (split_mode && query < Nq && (!EXACT || mine)) {
+    if (split_mode && query < Nq) {
       const size_t prow = ((size_t)split * ex.BH + bh) * Nq + query;
       float* orow = ex.ws_o + prow * C::D;
 #pragma unroll
@@ -811,9 +818,8 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
           ov.w = acc[db][4 * a + 3] * inv;
           *(float4*)(orow + 32 * db + 8 * a + 4 * h) = ov;
         }
-      if (h == 0)
-        ex.ws_lse[prow] = jumped ? __builtin_nanf("") : (empty ? -INFINITY : (m + __log2f(lt)) * kLn2);
-    } else if (query < Nq && (!EXACT || mine)) {  // the recompute pass stores only marked rows
+      if (h == 0) ex.ws_lse[prow] = empty ? -INFINITY : (m + __log2f(lt)) * kLn2;
+    } else if (query < Nq) {
       uint16_t* orow = o + hoff + (size_t)query * C::D;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -824,43 +830,21 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
           for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[db][4 * a + e] * inv);
           *(u32x2*)(orow + 32 * db + 8 * a + 4 * h) = __builtin_bit_cast(u32x2, ov);
         }
-      // a row whose scores jumped past the fixed reference is marked (NaN
-      // LSE) for the recompute pass
-      if (h == 0) lse[(size_t)bh * Nq + query] = jumped ? __builtin_nanf("") : (m + __log2f(lt)) * kLn2;
+      if (h == 0) lse[(size_t)bh * Nq + query] = (m + __log2f(lt)) * kLn2;
     }
   }
-  if (EXACT) return false;
-  // any row of the unit marked? (the flags are rewritten only after this
-  // barrier, by the recompute pass)
-  const bool wave_jumped = __builtin_amdgcn_ballot_w64(unit_jumped) != 0;  // every lane votes
-  if (lane == 0) wave_marked[w] = wave_jumped;
-  __syncthreads();
-  int any = 0;
-#pragma unroll
-  for (int ww = 0; ww < C::NW; ++ww) any |= wave_marked[ww];
-  return __builtin_amdgcn_readfirstlane(any) != 0;
 }
 
-// The forward kernel: the fast pass over one work unit, then -- only when it
-// marked a row, i.e. a row whose scores jumped past its fixed exponent
-// reference -- the exact recompute pass over the same unit, in the same
-// workgroup.  The marks are read back from LSE after a workgroup barrier,
-// which makes the fast pass's global stores visible to every wave of the
-// workgroup.
+// The forward kernel: one work unit per workgroup.
 template <class C, bool CAUSAL, bool EXT = false>
 __global__ void __launch_bounds__(C::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
                    int N, int T_r, int units_per_head, int num_units, int per_xcd, float c,
                    unsigned int qsign, ExtArgs ex) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDSB + 4 * C::NW];
-  unsigned char LDS_AS* lds = (unsigned char LDS_AS*)smem;
-  if (fwd_unit<C, CAUSAL, false, EXT>(q, k, v, o, lse, N, T_r, units_per_head, num_units, per_xcd, c, qsign, ex,
-                                      lds)) {
-    __syncthreads();
-    fwd_unit<C, CAUSAL, true, EXT>(q, k, v, o, lse, N, T_r, units_per_head, num_units, per_xcd, c, qsign, ex,
-                                   lds);
-  }
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDSB];
+  fwd_unit<C, CAUSAL, EXT>(q, k, v, o, lse, N, T_r, units_per_head, num_units, per_xcd, c, qsign, ex,
+                           (unsigned char LDS_AS*)smem);
 }
 
 // ---------------------------------------------------------------------------

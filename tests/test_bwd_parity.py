@@ -10,10 +10,11 @@ with reference R, measured against the tensor's own scale
 ``s = max(1, max|R|)`` (absolute for gradients below 1, as for the forward
 with N(0,1) inputs): max|G - R| <= BWD_MAX * s and mean|G - R| <= BWD_MEAN * s.
 The kernel rounds P and dS to bf16 for the second matrix products (unit
-roundoff 2^-9 each), rounds the result to bf16 (2^-9), and takes O and LSE
-from the bf16 forward (O rounded to bf16 enters D = O . dO); with
-cancellation in the sums over keys of dS (its rows sum to zero) an error
-of a few bf16 ulps of the largest term is what remains.
+roundoff u = 2^-8 each: bf16 keeps 8 significant bits, so one ulp at 1.0 is
+2^-7), rounds the result to bf16 (u again), and takes O and LSE from the
+bf16 forward (O rounded to bf16 enters D = O . dO); with cancellation in the
+sums over keys of dS (its rows sum to zero) an error of a few units of
+roundoff of the largest term is what remains.
 """
 
 import numpy as np
@@ -27,7 +28,7 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-BWD_MAX = 1.6e-2   # max abs error / max |ref|   (4 bf16 ulps at 2^-8 each)
+BWD_MAX = 1.6e-2   # max abs error / max |ref|   (about 4 u = 4 * 2^-8, i.e. 2 bf16 ulps at 1.0)
 BWD_MEAN = 2.0e-3  # mean abs error / max |ref|
 
 

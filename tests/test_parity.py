@@ -183,8 +183,9 @@ def test_status_codes_through_binding():
 @pytest.mark.parametrize("causal", [False, True])
 def test_score_jump_recompute(d, causal):
     """Scores that rise far above the first key tile's maximum (here by ~70
-    in log2 units, past the fast kernel's fixed-reference slack) are redone
-    by the exact recompute pass; the result must still match the oracle."""
+    in log2 units, past the fixed reference's slack of 16) make the kernel
+    take the running-max step of the recurrence on those tiles; the result
+    must still match the oracle."""
     N = 700
     g = torch.Generator().manual_seed(d + causal)
     q = torch.ones(1, 2, N, d) + 0.1 * torch.randn(1, 2, N, d, generator=g)
@@ -201,7 +202,7 @@ def test_score_jump_recompute(d, causal):
 
 
 # (head, row) pairs whose scores jump at key 150: rows at lanes 11, 5, 11,
-# 31, 0 and 27 of their wave, and head 1 with one marked row (lane 12 of
+# 31, 0 and 27 of their wave, and head 1 with one jumping row (lane 12 of
 # wave 1, tile 1)
 JUMP_ROWS = [(0, 203), (0, 261), (0, 299), (0, 511), (0, 640), (0, 699), (1, 300)]
 # jumps that start inside the last, ragged key tile (keys 695..699 of 700),
@@ -214,9 +215,9 @@ TAIL_JUMP_ROWS = [(0, 697), (1, 699)]
 @pytest.mark.parametrize("causal", [False, True])
 def test_score_jump_some_rows(d, causal, rows, key0):
     """Only the listed rows see their scores rise by 60 nats from key key0
-    on, past the first key tile's reference: those rows alone are marked,
-    and each must be redone exactly however few of its tile's (or wave's)
-    rows are marked with it."""
+    on, past the first key tile's reference: those rows alone raise their
+    reference (the running-max step), however few rows of their tile (or
+    wave) rise with them, and the others keep theirs."""
     N = 700
     q, k, v = workloads.make_jump_qkv(1, 2, 2, N, N, d, rows, key0=key0, seed=31 + d)
     scale = 1.0 / math.sqrt(d)

@@ -1,8 +1,9 @@
 """Seeded random cases through every entry point against the fp64 oracles:
 shapes, masks, scales, head groupings, query offsets, windows and split
 counts are drawn per case (the case's seed names it), and some cases plant
-scores that jump by 60 nats for a few random rows, so that the exact
-recompute pass runs on rows scattered over lanes, waves and query tiles.
+scores that jump by 60 nats for a few random rows, so that the running-max
+step of the bf16 kernels runs for rows scattered over lanes, waves and query
+tiles.
 Tolerances are those of the dedicated parity tests: the bf16 and fp32
 forward bounds (widened for the forward's sharper random scales where the
 rounding model gives more, see _forward_tol), and for the backward max

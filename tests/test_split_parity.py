@@ -68,7 +68,8 @@ def _check(q, k, v, causal, offset, window, nsplit, what, partials=True):
         full = ~empty
         assert_close(wo[full], wl[full], po[full], pl[full], torch.bfloat16, what + " partials")
         # the merge kernel: the oracle's merge of the kernel's own partials,
-        # up to the final bf16 rounding of O (half an ulp, 2^-9 relative)
+        # up to the final bf16 rounding of O (half an ulp: at most 2^-8
+        # relative, bf16 keeping 8 significant bits)
         # and fp32 rounding of the weights and of LSE
         mo, ml = merge_partials_ref(wo, wl)
         assert np.all(np.abs(mo - o) <= 2.0 ** -8 * np.abs(mo) + 1e-5), what + " merge O"
@@ -126,8 +127,8 @@ def test_single_chunk_is_fa_fwd_ex_bitwise():
 
 def test_climbing_scores_take_the_exact_path():
     """Scores that climb by hundreds of nats along the keys: rows whose
-    later keys outgrow the first tile's reference are redone with exact
-    rescaling inside each chunk, partials included."""
+    later keys outgrow the first tile's reference take the running-max step
+    inside each chunk, partials included."""
     require_gpu()
     for d, T, S in ((128, 1, 4096), (64, 1, 4096), (128, 64, 2000)):
         q, k, v = _qkv(1, 4, 2, T, S, d, seed=d + T, ramp=300.0)
@@ -137,8 +138,8 @@ def test_climbing_scores_take_the_exact_path():
 @pytest.mark.parametrize("d", [64, 128])
 def test_score_jump_some_rows(d):
     """Only a few scattered rows see their scores rise by 60 nats at key 800,
-    inside the second of three chunks: those rows' partials of that chunk
-    are marked and redone (large-tile split path, then the merge)."""
+    inside the second of three chunks: those rows raise their reference in
+    that chunk's partial (large-tile split path, then the merge)."""
     require_gpu()
     rows = [(0, 100), (0, 131), (1, 257), (1, 299), (2, 200), (3, 163)]
     q, k, v = workloads.make_jump_qkv(1, 4, 2, 300, 1500, d, rows, key0=800, seed=51 + d)

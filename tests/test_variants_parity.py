@@ -162,8 +162,8 @@ EX_JUMP_ROWS = [(0, 100), (0, 131), (1, 257), (1, 299), (2, 200), (3, 163)]
 def test_score_jump_some_rows(d):
     """Only the rows in EX_JUMP_ROWS see their scores rise by 60 nats at key
     800 (past the reference of the first tile each of them sees), with
-    grouped heads, an offset and a window: those rows alone are marked and
-    redone."""
+    grouped heads, an offset and a window: those rows alone take the
+    running-max step."""
     require_gpu()
     B, Hq, Hkv, T, S = 1, 4, 2, 300, 1500
     q, k, v = workloads.make_jump_qkv(B, Hq, Hkv, T, S, d, EX_JUMP_ROWS, key0=800, seed=41 + d)

@@ -108,16 +108,16 @@ def make_qkv_device(B, Hq, Hkv, T, S, d, dtype=torch.bfloat16, seed=0, device="c
     return q, k, v
 
 
-def make_jump_qkv(B, Hq, Hkv, T, S, d, rows, key0, lift=60.0, seed=0):
+def make_jump_qkv(B, Hq, Hkv, T, S, d, rows, key0, lift=60.0, seed=0, key1=None):
     """Q [B, Hq, T, d], K and V [B, Hkv, S, d] (bf16, CPU) in which only the
     chosen query rows see their scores jump.  Q, then K, then V are drawn
     i.i.d. N(0, 1) in float32 from a CPU generator seeded with ``seed``, then
     a unit vector u (a fourth draw, normalised) is projected out of every
     query and key row; each (head, row) pair in ``rows`` gets
     sqrt(lift * sqrt(d)) u added to its query, and every key from ``key0`` on
-    gets the same.  With the scale 1/sqrt(d) the chosen rows' scores rise by
-    ``lift`` nats at key ``key0``; the other rows hold no component along u
-    (up to the bf16 rounding)."""
+    (up to ``key1``, exclusive, when given) gets the same.  With the scale
+    1/sqrt(d) the chosen rows' scores rise by ``lift`` nats on those keys;
+    the other rows hold no component along u (up to the bf16 rounding)."""
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
     q = torch.randn((B, Hq, T, d), generator=g, dtype=torch.float32)
@@ -130,7 +130,7 @@ def make_jump_qkv(B, Hq, Hkv, T, S, d, rows, key0, lift=60.0, seed=0):
     a = math.sqrt(lift * math.sqrt(d))
     for h, t in rows:
         q[:, h, t] += a * u
-    k[:, :, key0:] += a * u
+    k[:, :, key0:key1] += a * u
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
