@@ -66,7 +66,8 @@ enum fa_status {
     FA_ERR_ALIAS = 5,     /* O or LSE overlaps Q, K, V or each other        */
     FA_ERR_LAUNCH = 6,    /* the HIP launch reported an error               */
     FA_ERR_ALIGN = 7,     /* a pointer is not aligned to 16 bytes           */
-    FA_ERR_VARIANT = 8    /* fa_fwd_ex/_split: Hq % Hkv, S == 0, offset, window, nsplit */
+    FA_ERR_VARIANT = 8,   /* fa_fwd_ex/_split: Hq % Hkv, S == 0, offset, window, nsplit */
+    FA_ERR_SCRATCH = 9    /* fa_fwd_split_noalloc: partials exceed FA_SPLIT_NOALLOC_BYTES */
 };
 
 /*
@@ -205,6 +206,27 @@ int fa_check_args_ex(const void* q, const void* k, const void* v, const void* o,
 int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int T,
                  int S, int d, float scale, int causal, int offset, int window, int nsplit, float* ws_o,
                  float* ws_lse, hipStream_t stream);
+
+/*
+ * fa_fwd_split for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving (decode) loops, harnesses that forbid
+ * hipMalloc.  Same arguments, result and errors as fa_fwd_split without
+ * ws_o / ws_lse: the partials go to a device array the library holds,
+ * FA_SPLIT_NOALLOC_BYTES bytes per device, held from the first call on a
+ * device (which looks up its address) until the process ends.  Nothing is
+ * allocated, freed or memset by the call.
+ *   Limit: G * B * Hq * T * (d + 1) * 4 <= FA_SPLIT_NOALLOC_BYTES, with
+ *   G = fa_split_chunks(S, nsplit) (a single chunk uses no scratch);
+ *   larger calls return FA_ERR_SCRATCH before any launch.
+ *   Sharing: every call on one device uses the same array, which keeps the
+ *   last call's partials; calls that overlap in time on one device (two
+ *   streams, two threads) race on it and must be serialised by the caller.
+ * FA_ERR_LAUNCH also reports a failure to find the array's device address.
+ */
+#define FA_SPLIT_NOALLOC_BYTES (32u << 20)
+int fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                         int T, int S, int d, float scale, int causal, int offset, int window, int nsplit,
+                         hipStream_t stream);
 
 /* Number of key chunks G that fa_fwd_split uses for S keys and a requested
  * nsplit (1 for S <= 0 or nsplit < 1); sizes its workspaces. */

@@ -1,7 +1,7 @@
 """ctypes binding of the C ABI in ``include/fa.h`` (argument marshalling only).
 
 The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_fwd_ex``, ``fa_fwd_split``,
-``fa_bwd``, ``fa_strerror``, ``fa_check_args``, ``fa_check_args_ex``,
+``fa_fwd_split_noalloc``, ``fa_bwd``, ``fa_strerror``, ``fa_check_args``, ``fa_check_args_ex``,
 ``fa_check_args_split``, ``fa_split_chunks`` and ``fa_bwd_check_args`` have
 the names and argument order of the C entry points; tensors are passed
 as their device pointers and streams as HIP stream handles.  Every step of
@@ -25,9 +25,11 @@ FA_ERR_ALIAS = 5
 FA_ERR_LAUNCH = 6
 FA_ERR_ALIGN = 7
 FA_ERR_VARIANT = 8
+FA_ERR_SCRATCH = 9
+FA_SPLIT_NOALLOC_BYTES = 32 << 20
 
-EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_split", "fa_bwd", "fa_strerror", "fa_check_args",
-            "fa_check_args_ex", "fa_check_args_split", "fa_split_chunks", "fa_bwd_check_args")
+EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_split", "fa_fwd_split_noalloc", "fa_bwd", "fa_strerror",
+            "fa_check_args", "fa_check_args_ex", "fa_check_args_split", "fa_split_chunks", "fa_bwd_check_args")
 
 _lib = None
 
@@ -69,6 +71,8 @@ def load_library(path=None):
     lib.fa_check_args_ex.restype = i
     lib.fa_fwd_split.argtypes = [vp] * 5 + [i, i, i, i, i, i, f, i, i, i, i, vp, vp, vp]
     lib.fa_fwd_split.restype = i
+    lib.fa_fwd_split_noalloc.argtypes = [vp] * 5 + [i, i, i, i, i, i, f, i, i, i, i, vp]
+    lib.fa_fwd_split_noalloc.restype = i
     lib.fa_check_args_split.argtypes = [vp] * 5 + [i, i, i, i, i, i, f, i, i, i, i, vp, vp]
     lib.fa_check_args_split.restype = i
     lib.fa_split_chunks.argtypes = [i, i]
@@ -125,6 +129,14 @@ def fa_fwd_split(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, wi
     return load_library().fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq), int(Hkv),
                                        int(T), int(S), int(d), float(scale), int(causal), int(offset), int(window),
                                        int(nsplit), _ptr(ws_o), _ptr(ws_lse), _stream(stream))
+
+
+def fa_fwd_split_noalloc(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window, nsplit, stream=None):
+    """C ``fa_fwd_split_noalloc``: ``fa_fwd_split`` with its partials in the
+    library's static device scratch (no workspaces, nothing allocated)."""
+    return load_library().fa_fwd_split_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(Hq),
+                                               int(Hkv), int(T), int(S), int(d), float(scale), int(causal),
+                                               int(offset), int(window), int(nsplit), _stream(stream))
 
 
 def fa_check_args_split(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window, nsplit, ws_o,

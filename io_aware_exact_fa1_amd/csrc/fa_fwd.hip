@@ -1056,6 +1056,7 @@ extern "C" const char* fa_strerror(int status) {
     case FA_ERR_LAUNCH: return "HIP kernel launch failed";
     case FA_ERR_ALIGN: return "pointer not aligned (16 bytes for q/k/v/o, 4 for lse)";
     case FA_ERR_VARIANT: return "inconsistent heads, offset or window (fa_fwd_ex)";
+    case FA_ERR_SCRATCH: return "partials larger than the static scratch (fa_fwd_split_noalloc)";
     default: return "unknown status";
   }
 }

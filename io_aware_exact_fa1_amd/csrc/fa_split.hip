@@ -1,6 +1,7 @@
 // Split-KV attention forward (flash-decoding) for MI355X (gfx950): the
 // small-tile partial kernel, the merge kernel and the C entry points
-// fa_fwd_split, fa_check_args_split and fa_split_chunks.
+// fa_fwd_split, fa_fwd_split_noalloc, fa_check_args_split and
+// fa_split_chunks.
 //
 // What is computed: "15. FlashAttention" (inference.shantanugoel.com),
 // section "Decode is different: flash-decoding": the keys are cut into
@@ -14,9 +15,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_device.h"
 #include "fa_host.h"
+
+// Scratch of fa_fwd_split_noalloc: the fp32 partials of a call (ws_o, then
+// ws_lse).  Every device the library runs on holds its own copy until the
+// process ends; all calls on a device share it.  In host code `scratch` is
+// only a handle: its device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[FA_SPLIT_NOALLOC_BYTES];
 
 namespace {
 
@@ -453,6 +462,29 @@ extern "C" int fa_check_args_split(const void* q, const void* k, const void* v, 
   return FA_OK;
 }
 
+namespace {
+
+// Device address of the scratch on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
 extern "C" int fa_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                             int Hkv, int T, int S, int d, float scale, int causal, int offset, int window,
                             int nsplit, float* ws_o, float* ws_lse, hipStream_t stream) {
@@ -493,4 +525,33 @@ extern "C" int fa_fwd_split(const void* q, const void* k, const void* v, void* o
   if (d == 128) launch_merge<128>(ws_o, ws_lse, o, lse, rows, g, stream);
   else launch_merge<64>(ws_o, ws_lse, o, lse, rows, g, stream);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                    int Hq, int Hkv, int T, int S, int d, float scale, int causal, int offset,
+                                    int window, int nsplit, hipStream_t stream) {
+  const int st = host_check_ex(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window);
+  if (st != FA_OK) return st;
+  if (nsplit < 1 || nsplit > 4096) return FA_ERR_VARIANT;
+  const long long rows = (long long)B * Hq * T;
+  if (rows == 0) return FA_OK;
+  const int g = fa_split_chunks(S, nsplit);
+  float* ws_o = nullptr;
+  float* ws_lse = nullptr;
+  if (g > 1) {
+    // ws_o [G, B, Hq, T, d] then ws_lse [G, B, Hq, T], fp32 (rows <= 2^40,
+    // G <= 4096, d + 1 <= 129: the product fits 64 bits)
+    const unsigned long long need = (unsigned long long)g * (unsigned long long)rows * (unsigned)(d + 1) * 4ull;
+    if (need > (unsigned long long)FA_SPLIT_NOALLOC_BYTES) return FA_ERR_SCRATCH;
+    void* p = nullptr;
+    const int sst = device_scratch(&p);
+    if (sst != FA_OK) return sst;
+    ws_o = (float*)p;
+    ws_lse = ws_o + (size_t)g * (size_t)rows * d;
+  }
+  // the same checks and kernels as fa_fwd_split, on the scratch (every
+  // partial the merge reads is written first by the partial kernel, so
+  // nothing needs clearing between calls)
+  return fa_fwd_split(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, offset, window, nsplit, ws_o, ws_lse,
+                      stream);
 }

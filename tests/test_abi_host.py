@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted(["fa_bwd", "fa_bwd_check_args", "fa_check_args", "fa_check_args_ex",
                                            "fa_check_args_split", "fa_fwd", "fa_fwd_ex", "fa_fwd_f32",
-                                           "fa_fwd_split", "fa_split_chunks", "fa_strerror"])
+                                           "fa_fwd_split", "fa_fwd_split_noalloc", "fa_split_chunks",
+                                           "fa_strerror"])
 
 
 def test_binding_exports_match_the_header():
@@ -43,7 +44,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_strerror_covers_codes():
-    for code in range(0, 9):
+    for code in range(0, 10):
         s = fa.fa_strerror(code)
         assert s and s != "unknown status", code
     assert fa.fa_strerror(99) == "unknown status"
@@ -250,3 +251,26 @@ def test_split_rejects_launches_past_32_bit_work_items():
     st = fa.fa_check_args_split(P[0], P[1], P[2], P[3], P[4], 4096, 64, 64, 1, 8192, 128, 0.1, 1, 8191, 0, 32,
                                 P[5], P[6])
     assert st == fa.FA_OK
+
+
+def test_split_noalloc_rejects_on_the_host():
+    """The argument checks of fa_fwd_split, then the scratch limit: partials
+    of G * B * Hq * T * (d + 1) * 4 bytes beyond FA_SPLIT_NOALLOC_BYTES are
+    refused before any HIP call."""
+    text = open(HEADER).read()
+    assert re.search(r"#define FA_SPLIT_NOALLOC_BYTES \(32u << 20\)", text)
+    assert fa.FA_SPLIT_NOALLOC_BYTES == 32 << 20
+    call = fa.fa_fwd_split_noalloc
+    assert call(Q, K, V, O, L, 1, 2, 2, 1, 1000, 128, 0.1, 1, 999, 0, 0, 0) == fa.FA_ERR_VARIANT    # nsplit
+    assert call(Q, K, V, O, L, 1, 3, 2, 1, 1000, 128, 0.1, 1, 999, 0, 4, 0) == fa.FA_ERR_VARIANT    # Hq % Hkv
+    assert call(Q, K, V, O, L, 1, 2, 2, 1, 1000, 80, 0.1, 1, 999, 0, 4, 0) == fa.FA_ERR_HEAD_DIM
+    assert call(None, None, None, None, None, 0, 2, 2, 1, 1000, 128, 0.1, 1, 999, 0, 4, 0) == fa.FA_OK
+    # 64 query heads x 4096 rows in 4 chunks of d = 128: 4 * 64 * 4096 * 129 * 4 bytes = 541 MB
+    P = [(i + 1) << 44 for i in range(5)]
+    assert call(P[0], P[1], P[2], P[3], P[4], 1, 64, 64, 4096, 4096, 128, 0.1, 1, 0, 0, 4, 0) == fa.FA_ERR_SCRATCH
+    # the largest decode that fits: G * rows * (d + 1) * 4 <= 32 MiB
+    G, d = 32, 128
+    rows = (32 << 20) // (G * (d + 1) * 4)
+    assert call(P[0], P[1], P[2], P[3], P[4], 1, rows + 1, 1, 1, 32 * 128, d, 0.1, 1, 32 * 128 - 1, 0, G,
+                0) == fa.FA_ERR_SCRATCH
+
