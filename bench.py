@@ -98,6 +98,12 @@ def parse():
                    help="time every workload of the five configs (one JSON line each), graph-replayed and eager")
     p.add_argument("--graph", action="store_true",
                    help="--shapes: capture the timed calls in one HIP graph (no host launch overhead)")
+    p.add_argument("--tile", default=None,
+                   help="--shapes: 'Br,Bc' of the library under test (FA_MI355X_LIB), for the tile-stream byte "
+                        "model (default: the library's own 256 x 64 at d = 128, 256 x 128 at d = 64)")
+    p.add_argument("--memory", default=None,
+                   help="'B,H,d,causal;N1,N2,...': peak device memory and time of fa_fwd against an unfused "
+                        "matmul-softmax-matmul (torch) at each N")
     p.add_argument("--copy-cal", action="store_true",
                    help="run only a plain device copy of 1 GiB (5 times), to calibrate the HBM "
                         "byte counters (FETCH_SIZE / WRITE_SIZE) of a profiler run")
@@ -317,14 +323,15 @@ def shape_sweep(args):
             flops = 4.0 * B * H * pairs * d
         else:
             flops = 4.0 * B * H * N * N * d / (2 if causal else 1)
-        br, bc = 256, (64 if d == 128 else 128)
+        br, bc = (256, (64 if d == 128 else 128)) if not args.tile else (int(x) for x in args.tile.split(","))
         print(json.dumps({"shape": {"B": B, "H": H, "N": N, "d": d, "causal": bool(causal), "Hkv": hkv,
                                     "window": window, "T": T, "entry": entry, "nsplit": nsplit, "chunks": G},
                           "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
                           "kv_gbs": round(2.0 * B * hkv * N * d * 2 / ms / 1e6, 1),
                           "once_bytes": workloads.hbm_once_bytes(B, H, N, d),
                           "stream_bytes": workloads.tile_stream_bytes(B, H, N, d, br, bc, bool(causal)),
-                          "tile": {"Br": br, "Bc": bc}, "graph": args.graph, "graph_equals_eager": graph_ok}),
+                          "tile": {"Br": br, "Bc": bc}, "library": os.path.basename(fa.load_library()._name),
+                          "graph": args.graph, "graph_equals_eager": graph_ok}),
               flush=True)
         if args.graph:
             del graph
@@ -467,6 +474,66 @@ def config_sweep(args):
         del q, k, v, o, lse
 
 
+def memory_compare(args):
+    """Peak device memory (beyond the inputs) and time of one fa_fwd call and
+    of the unfused computation it replaces -- S = Q K^T materialised, the
+    softmax in fp32, then P V -- at each listed N (one JSON line per N).
+    The unfused form is torch matrix products and softmax: a reference
+    point for the memory argument of the pages, not part of the library."""
+    import torch
+    import io_aware_exact_fa1_amd as fa
+    import workloads
+
+    fa.load_library()
+    head, ns = args.memory.split(";")
+    B, H, d, causal = (int(x) for x in head.split(","))
+    scale = 1.0 / math.sqrt(d)
+    dev = torch.device("cuda:0")
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for N in (int(x) for x in ns.split(",")):
+        q, k, v = (x.to(dev) for x in workloads.make_qkv(B, H, N, d, torch.bfloat16, 2000 + N))
+        torch.cuda.synchronize()
+        res = {"B": B, "H": H, "N": N, "d": d, "causal": bool(causal)}
+        for name in ("fa_fwd", "unfused"):
+            def run():
+                if name == "fa_fwd":
+                    return fa.forward(q, k, v, causal=bool(causal), scale=scale)
+                kt = k.transpose(-2, -1).contiguous()      # (a contiguous right operand for the bf16 product)
+                s = torch.matmul(q, kt).float() * scale    # [B, H, N, N]
+                if causal:
+                    s.masked_fill_(torch.ones(N, N, dtype=torch.bool, device=dev).triu_(1), float("-inf"))
+                lse = torch.logsumexp(s, dim=-1)
+                p = torch.softmax(s, dim=-1).to(torch.bfloat16)
+                del s
+                return torch.matmul(p, v), lse
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            base = torch.cuda.memory_allocated()
+            torch.cuda.reset_peak_memory_stats()
+            out = run()
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated() - base
+            del out
+            ms = timed(lambda: run())
+            res[name] = {"peak_bytes_beyond_inputs": int(peak), "ms": round(ms, 4)}
+            log(f"[memory] N={N} {name}: peak {peak / 2**20:.1f} MiB beyond the inputs, {ms:.3f} ms")
+        res["output_bytes"] = B * H * N * (d * 2 + 4)
+        print(json.dumps(res), flush=True)
+        del q, k, v
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -483,6 +550,9 @@ def main():
         return
     if args.shapes:
         shape_sweep(args)
+        return
+    if args.memory:
+        memory_compare(args)
         return
 
     import torch

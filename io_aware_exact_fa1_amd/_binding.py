@@ -44,12 +44,14 @@ class FaError(RuntimeError):
 
 def load_library(path=None):
     """Load the HIP library (once).  torch is imported first so that the
-    library binds to the HIP runtime torch already loaded."""
+    library binds to the HIP runtime torch already loaded.  The library is
+    the one built next to this file, or the build that the environment
+    variable FA_MI355X_LIB names (e.g. a tile-shape variant)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
     import torch  # noqa: F401  (must precede the CDLL: one HIP runtime per process)
-    p = path or LIB_PATH
+    p = path or os.environ.get("FA_MI355X_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(
             f"HIP library {p} is not built: run `python -m io_aware_exact_fa1_amd.build` "

@@ -5,6 +5,10 @@ Each source is compiled to its own object in parallel, then the objects are
 linked into the shared library.
 
 Usage:  python -m io_aware_exact_fa1_amd.build   (or call ``build()``).
+        python -m io_aware_exact_fa1_amd.build --out PATH -D FA_D64_BC=64 -D FA_D64_NW=4
+            builds a tile-shape variant elsewhere (B_c keys per K/V tile and
+            NW waves of 32 query rows, per head dimension); the binding loads
+            it when FA_MI355X_LIB names it.
 """
 
 import concurrent.futures
@@ -85,5 +89,18 @@ def build(verbose=False, extra=(), out=None, sources=None):
         shutil.rmtree(tmpdir, ignore_errors=True)
 
 
+def main(argv=None):
+    import argparse
+    ap = argparse.ArgumentParser(description="build the HIP library for gfx950")
+    ap.add_argument("--out", default=None, help="library path (default: next to this file)")
+    ap.add_argument("-D", dest="defines", action="append", default=[],
+                    help="preprocessor definition, e.g. FA_D64_BC=64 (tile-shape variants)")
+    a = ap.parse_args(argv)
+    out = a.out
+    if out:
+        os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    print(build(verbose=True, extra=[f"-D{x}" for x in a.defines], out=out))
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    main()

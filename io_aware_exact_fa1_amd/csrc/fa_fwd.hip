@@ -86,14 +86,14 @@ constexpr float kSlack = 16.0f;
 constexpr float kJumpSum = 0x1p16f;  // 2^kSlack
 
 // ---------------------------------------------------------------------------
-// Tile configuration of the bf16 kernel: 8 waves of 32 query rows each
-// (two waves per SIMD), key tiles of BC rows, a ring of NST LDS stages.
+// Tile configuration of the bf16 kernel: NW waves of 32 query rows each
+// (8: two waves per SIMD), key tiles of BC rows, a ring of NST LDS stages.
 // LDS layout: the K tiles of the NST stages, then the V tiles.
-template <int D_, int BC_>
+template <int D_, int BC_, int NW_ = 8>
 struct Cfg {
   static constexpr int D = D_;             // head dimension
   static constexpr int BC = BC_;           // keys per K/V tile (B_c)
-  static constexpr int NW = 8;             // waves per workgroup
+  static constexpr int NW = NW_;           // waves per workgroup
   static constexpr int BR = 32 * NW;       // query rows per tile (B_r)
   static constexpr int ROWB = D * 2;       // bytes of one K/V row
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
@@ -103,7 +103,8 @@ struct Cfg {
   static constexpr int VBASE = NST * KT;   // start of the V tiles in LDS
   static constexpr int LDSB = 2 * NST * KT;
   static constexpr int NINST = KT / 1024;  // 1 KB copies per matrix per tile
-  static constexpr int NCW = NW / 2;       // waves copying one matrix (K: waves 0..3, V: 4..7)
+  static constexpr int NCW = NW / 2;       // waves copying one matrix (K: the first half, V: the second)
+  static_assert(NW == 4 || NW == 8, "workgroup of 4 or 8 waves");
   static constexpr int NI = NINST / NCW;   // copy instructions per wave per tile
   static constexpr int KB = D / 16;        // 16-deep k-steps of Q K^T
   static constexpr int DB = D / 32;        // 32-dim output blocks
@@ -302,11 +303,19 @@ __device__ __forceinline__ float tile_rowmax(const f32x16 (&s)[C::SB]) {
 // to the running max m_new = max(m, mxs), and l and acc are multiplied by
 // exp2(m - m_new).  Other rows keep every bit as it is, so that a row's
 // result never depends on what other rows of its wave see.
+// A row's running sums: l of the unrounded fp32 weights (LSE = m + log2 l)
+// and lb of the same weights rounded to bf16, the ones P V multiplies (O =
+// acc / lb, so that the weights applied to V sum to exactly one).
+struct RowSums {
+  float l, lb;
+};
+
 template <class C>
-__device__ __forceinline__ void raise_ref(bool up, float mxs, float& m, float& lsum, f32x16 (&acc)[C::DB]) {
+__device__ __forceinline__ void raise_ref(bool up, float mxs, float& m, RowSums& sums, f32x16 (&acc)[C::DB]) {
   const float m_new = up ? __builtin_fmaxf(m, mxs) : m;
   const float alpha = m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-  lsum *= alpha;
+  sums.l *= alpha;
+  sums.lb *= alpha;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -334,7 +343,7 @@ __device__ __forceinline__ float tile_exp(f32x16 (&s)[C::SB], float c, float mre
 // N, and keys after the query when causal, get -inf, i.e. weight exactly 0;
 // with a sliding window (wnd > 0) also keys before query - wnd + 1),
 // exponent reference, P = exp2(S*c - m_ref) into the bf16 operand pb, row
-// sum of the unrounded weights into lsum.
+// sums of the unrounded weights and of the bf16 weights into sums.
 //  * FIRST / MASK tiles compute their row max.  The reference is the max of
 //    the row's first tile with a visible key (a row that has seen none yet
 //    uses the safe reference 0); a row whose max in a masked tile rises more
@@ -349,7 +358,7 @@ __device__ __forceinline__ float tile_exp(f32x16 (&s)[C::SB], float c, float mre
 //    reference).
 template <class C, bool CAUSAL, bool MASK, bool FIRST, class Rescore>
 __device__ __forceinline__ void tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB],
-                                             float& m, float& lsum, int k0, int qw0, int N, float c, int lane,
+                                             float& m, RowSums& sums, int k0, int qw0, int N, float c, int lane,
                                              int wnd, Rescore&& rescore) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
@@ -380,7 +389,7 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
     const float mxs = (mx == -INFINITY) ? -INFINITY : mx * c;  // c > 0
     const bool had_ref = m != -INFINITY;
     const bool up = had_ref && mxs > m + kSlack;  // (the same in both halves of a row)
-    if (!FIRST && __builtin_amdgcn_ballot_w64(up) != 0) raise_ref<C>(up, mxs, m, lsum, acc);
+    if (!FIRST && __builtin_amdgcn_ballot_w64(up) != 0) raise_ref<C>(up, mxs, m, sums, acc);
     // the reference is the max of the first tile with a visible key
     m = had_ref ? m : mxs;
   }
@@ -394,18 +403,31 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
       const bool up = half_max(ts) > kJumpSum;  // either half of the row
       rescore();
       const float mx = tile_rowmax<C>(s);
-      raise_ref<C>(up, mx * c, m, lsum, acc);
+      raise_ref<C>(up, mx * c, m, sums, acc);
       ts = tile_exp<C>(s, c, m);
     }
   }
-  lsum += ts;
+  sums.l += ts;
 #pragma unroll
   for (int kb2 = 0; kb2 < C::PB; ++kb2) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) pb[kb2][j] = (__bf16)s[kb2 >> 1][8 * (kb2 & 1) + j];
     pin(pb[kb2]);
   }
-  pin(lsum);
+  // sum of the bf16 weights: v_dot2c_f32_bf16 against (1, 1), two chains
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  float tb[2] = {0.f, 0.f};
+#pragma unroll
+  for (int kb2 = 0; kb2 < C::PB; ++kb2) {
+    tb[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 0, 1), one2, tb[0], false);
+    tb[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 2, 3), one2, tb[1], false);
+    tb[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 4, 5), one2, tb[0], false);
+    tb[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 6, 7), one2, tb[1], false);
+  }
+  sums.lb += tb[0] + tb[1];
+  pin(sums.l);
+  pin(sums.lb);
 }
 
 // Arguments of the variants (EXT = true): query rows T and key rows S per
@@ -543,7 +565,8 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     // key tile of step j (wave-uniform)
     auto ktile = [&](int j) __attribute__((always_inline)) { return desc ? klast - j : kt0 + j; };
 
-    float m = -INFINITY, lsum = 0.f;
+    float m = -INFINITY;
+    RowSums sums{0.f, 0.f};
     f32x16 acc[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -619,7 +642,7 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     auto vphase = [&](int j, int kst0, int dst, int kst1, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
       constexpr bool FIRST = decltype(first_tag)::value;
-      tile_softmax<C, CAUSAL, MASK, FIRST>(s, p, acc, m, lsum, ktile(j) * C::BC, qoff + qw0, Nk, c, lane, wnd,
+      tile_softmax<C, CAUSAL, MASK, FIRST>(s, p, acc, m, sums, ktile(j) * C::BC, qoff + qw0, Nk, c, lane, wnd,
                                            [&]() __attribute__((always_inline)) { rescore_at(kst0); });
       __builtin_amdgcn_sched_barrier(0);
       if (VC) {
@@ -673,7 +696,7 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         constexpr bool LAG = decltype(lag_tag)::value;
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool FIRST = decltype(first_tag)::value;
-        tile_softmax<C, CAUSAL, MASK, FIRST>(s, p, acc, m, lsum, ktile(j) * C::BC, qoff + qw0, Nk, c, lane, wnd,
+        tile_softmax<C, CAUSAL, MASK, FIRST>(s, p, acc, m, sums, ktile(j) * C::BC, qoff + qw0, Nk, c, lane, wnd,
                                              [&]() __attribute__((always_inline)) { rescore_at(s0); });
         __builtin_amdgcn_sched_barrier(0);
         const int ct = LAG ? j + 2 : j + 3;  // the tile this wave copies now
@@ -799,10 +822,11 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     }
 
     // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
-    const float lt = half_sum(lsum);
+    const float lt = half_sum(sums.l);
+    const float ltb = half_sum(sums.lb);
     // (split-KV: no visible key in this chunk -> O_g = 0, LSE_g = -inf)
     const bool empty = EXT && !(lt > 0.f);
-    const float inv = empty ? 0.f : 1.f / lt;
+    const float inv = empty ? 0.f : 1.f / ltb;
     const int query = qw0 + l32;
     if (split_mode && query < Nq) {
       const size_t prow = ((size_t)split * ex.BH + bh) * Nq + query;
@@ -943,14 +967,24 @@ int check_ex(const void* q, const void* k, const void* v, const void* o, const f
   return FA_OK;
 }
 
+// Tile shapes (B_c keys per K/V tile, NW waves of 32 query rows: B_r = 32 NW).
+// The defaults are the library's; other values build the variants that the
+// tile-size sweep measures (where the LDS ring, the registers and the copy
+// mapping allow them: the static_asserts of Cfg).
 #ifndef FA_D128_BC
 #define FA_D128_BC 64
 #endif
 #ifndef FA_D64_BC
 #define FA_D64_BC 128
 #endif
-using CfgD128 = Cfg<128, FA_D128_BC>;
-using CfgD64 = Cfg<64, FA_D64_BC>;
+#ifndef FA_D128_NW
+#define FA_D128_NW 8
+#endif
+#ifndef FA_D64_NW
+#define FA_D64_NW 8
+#endif
+using CfgD128 = Cfg<128, FA_D128_BC, FA_D128_NW>;
+using CfgD64 = Cfg<64, FA_D64_BC, FA_D64_NW>;
 
 }  // namespace
 

@@ -70,6 +70,66 @@ def test_n8192_d64_peaky():
     _sampled_case(workloads.get("n8192_d64_peaky"), n_heads=4, n_rows=256)
 
 
+def _oracle_heads(q, k, v, scale, causal, heads):
+    """The fp64 oracle (attention_ref, whole heads) for the listed (b, h)
+    pairs: one head per task on a pool of host threads, BLAS held to one
+    thread per task (numpy releases the GIL in its products and loops)."""
+    import concurrent.futures
+    import os
+
+    import threadpoolctl
+
+    def one(bh):
+        b, h = bh
+        return attention_ref(f64(q[b, h]), f64(k[b, h]), f64(v[b, h]), scale, causal)
+
+    workers = max(1, min(8, len(os.sched_getaffinity(0))))
+    with threadpoolctl.threadpool_limits(1, user_api="blas"):
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(one, heads))
+
+
+def _full_heads(w, q, k, v, o, lse, heads, what):
+    """O and LSE of whole heads against the oracle; the mean bound holds for
+    the listed heads together."""
+    refs = _oracle_heads(q, k, v, w.scale, w.causal, heads)
+    og = np.stack([f64(o[b, h]) for b, h in heads])
+    lg = np.stack([f64(lse[b, h]) for b, h in heads])
+    orf = np.stack([r[0] for r in refs])
+    lrf = np.stack([r[1] for r in refs])
+    assert_close(og, lg, orf, lrf, w.torch_dtype, what)
+
+
+def test_n4096_d128_causal_every_row():
+    """Every row of every head of the B=2 H=32 N=4096 d=128 causal workload
+    against the oracle (the tolerances' mean taken over the whole output)."""
+    w = workloads.get("n4096_d128_causal")
+    q, k, v = workloads.make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, w.k_mult)
+    say(w.name, "every row")
+    o, lse = run_gpu(q, k, v, w.causal, w.scale)
+    o, lse = o.cpu(), lse.cpu()
+    _full_heads(w, q, k, v, o, lse, [(b, h) for b in range(w.B) for h in range(w.H)], w.name + " every row")
+
+
+@pytest.fixture(scope="module")
+def _peaky_run():
+    w = workloads.get("n8192_d64_peaky")
+    q, k, v = workloads.make_qkv(w.B, w.H, w.N, w.d, w.torch_dtype, w.seed, w.k_mult)
+    say(w.name, "every row")
+    o, lse = run_gpu(q, k, v, w.causal, w.scale)
+    return w, q, k, v, o.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("b", range(8))
+def test_n8192_d64_peaky_every_row(_peaky_run, b):
+    """Every row of the B=8 H=32 N=8192 d=64 peaky workload against the
+    oracle, one batch entry (32 heads) per case: each case's mean bound
+    implies the bound for the whole output."""
+    w, q, k, v, o, lse = _peaky_run
+    say(w.name, "every row of batch entry", b)
+    _full_heads(w, q, k, v, o, lse, [(b, h) for h in range(w.H)], f"{w.name} b={b}")
+
+
 def test_longctx_n16384_d128_causal():
     # seeded subset of 2 heads x 256 query rows, rows 0 and N-1 included
     _sampled_case(workloads.get("longctx_n16384_d128_causal"), n_heads=2, n_rows=256)
