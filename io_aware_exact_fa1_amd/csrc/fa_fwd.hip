@@ -303,19 +303,30 @@ __device__ __forceinline__ float tile_rowmax(const f32x16 (&s)[C::SB]) {
 // to the running max m_new = max(m, mxs), and l and acc are multiplied by
 // exp2(m - m_new).  Other rows keep every bit as it is, so that a row's
 // result never depends on what other rows of its wave see.
-// A row's running sums: l of the unrounded fp32 weights (LSE = m + log2 l)
-// and lb of the same weights rounded to bf16, the ones P V multiplies (O =
-// acc / lb, so that the weights applied to V sum to exactly one).
+// A lane's running sums over its keys of a row: lh = l / 2, where l is the
+// sum of the unrounded fp32 weights (LSE = m + log2 l; kept halved, an exact
+// scaling, so that the heavy-tile test below is one compare), and
+// corr = sum of (bf16(p) - p) over the tiles where it was taken.  O divides
+// by l + corr, the sum of the bf16 weights that P V multiplies, so that a
+// row dominated by one key gets that key's V row up to the bf16 rounding
+// of O.  (With the reference fixed at the first tile's max, a dominant
+// later weight is 2^rise, not 1 as under the running max: dividing by the
+// unrounded l would carry its bf16 rounding, up to 2^-8 relative, into O.)
+// The correction is taken on a tile only when the lane's weights of the
+// tile exceed half of what it summed before (a "heavy" tile; the branch is
+// wave-uniform, the correction per lane): a weight of a tile left out is
+// less than half of its row's final sum, so its rounding moves O by less
+// than 2^-9 |v|, and the weights that dominate a row are always corrected.
 struct RowSums {
-  float l, lb;
+  float lh, corr;
 };
 
 template <class C>
 __device__ __forceinline__ void raise_ref(bool up, float mxs, float& m, RowSums& sums, f32x16 (&acc)[C::DB]) {
   const float m_new = up ? __builtin_fmaxf(m, mxs) : m;
   const float alpha = m_new > m ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-  sums.l *= alpha;
-  sums.lb *= alpha;
+  sums.lh *= alpha;
+  sums.corr *= alpha;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -343,7 +354,8 @@ __device__ __forceinline__ float tile_exp(f32x16 (&s)[C::SB], float c, float mre
 // N, and keys after the query when causal, get -inf, i.e. weight exactly 0;
 // with a sliding window (wnd > 0) also keys before query - wnd + 1),
 // exponent reference, P = exp2(S*c - m_ref) into the bf16 operand pb, row
-// sums of the unrounded weights and of the bf16 weights into sums.
+// sum of the unrounded weights and, on heavy tiles, the bf16 rounding
+// correction into sums.
 //  * FIRST / MASK tiles compute their row max.  The reference is the max of
 //    the row's first tile with a visible key (a row that has seen none yet
 //    uses the safe reference 0); a row whose max in a masked tile rises more
@@ -407,27 +419,31 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
       ts = tile_exp<C>(s, c, m);
     }
   }
-  sums.l += ts;
 #pragma unroll
   for (int kb2 = 0; kb2 < C::PB; ++kb2) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) pb[kb2][j] = (__bf16)s[kb2 >> 1][8 * (kb2 & 1) + j];
     pin(pb[kb2]);
   }
-  // sum of the bf16 weights: v_dot2c_f32_bf16 against (1, 1), two chains
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  float tb[2] = {0.f, 0.f};
+  const bool heavy = ts > sums.lh;
+  if (__builtin_amdgcn_ballot_w64(heavy) != 0) {
+    // heavy tile: sum of the bf16 weights, v_dot2c_f32_bf16 against (1, 1)
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float tb[2] = {0.f, 0.f};
 #pragma unroll
-  for (int kb2 = 0; kb2 < C::PB; ++kb2) {
-    tb[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 0, 1), one2, tb[0], false);
-    tb[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 2, 3), one2, tb[1], false);
-    tb[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 4, 5), one2, tb[0], false);
-    tb[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 6, 7), one2, tb[1], false);
+    for (int kb2 = 0; kb2 < C::PB; ++kb2) {
+      tb[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 0, 1), one2, tb[0], false);
+      tb[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 2, 3), one2, tb[1], false);
+      tb[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 4, 5), one2, tb[0], false);
+      tb[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 6, 7), one2, tb[1], false);
+    }
+    // (only the heavy lanes: a row's bits never depend on other rows)
+    sums.corr += heavy ? (tb[0] + tb[1]) - ts : 0.f;
   }
-  sums.lb += tb[0] + tb[1];
-  pin(sums.l);
-  pin(sums.lb);
+  sums.lh = fmaf(ts, 0.5f, sums.lh);  // (exact scaling by a power of two)
+  pin(sums.lh);
+  pin(sums.corr);
 }
 
 // Arguments of the variants (EXT = true): query rows T and key rows S per
@@ -822,8 +838,8 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     }
 
     // ---- epilogue: O = acc / l (bf16, RNE), LSE = (m + log2 l) * ln 2
-    const float lt = half_sum(sums.l);
-    const float ltb = half_sum(sums.lb);
+    const float lt = 2.f * half_sum(sums.lh);
+    const float ltb = lt + half_sum(sums.corr);
     // (split-KV: no visible key in this chunk -> O_g = 0, LSE_g = -inf)
     const bool empty = EXT && !(lt > 0.f);
     const float inv = empty ? 0.f : 1.f / ltb;
