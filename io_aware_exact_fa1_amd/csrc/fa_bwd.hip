@@ -135,21 +135,6 @@ __device__ __forceinline__ void copy_tile(const uint16_t* src, unsigned dst, int
   }
 }
 
-// Global -> LDS copy of 4 bytes per lane (global_load_lds_dword): lane i
-// writes LDS bytes [m0 + 4 i, m0 + 4 i + 4).
-__device__ __forceinline__ void lds_copy4(const void* src, unsigned lds_dst) {
-  const unsigned base = __builtin_amdgcn_readfirstlane(lds_dst);
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dword %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(base)
-      : "memory");
-}
-
 __device__ __forceinline__ bf16x8 lds_row(unsigned addr) {
   return *(const bf16x8 LDS_AS*)((const unsigned char LDS_AS*)0 + addr);
 }
@@ -433,18 +418,30 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const uint16_t* qh = q + hoff;
     const uint16_t* oh = dout + hoff;
     // stage of query tile i: (i - qt0) & 1
+    // Wave 0 loads L (lanes 0..31) and D (lanes 32..63) of the tile's 32
+    // queries into a register when the tile's copies are issued, and writes
+    // them to LDS (L times log2(e), once per query instead of once per lane
+    // that uses it) after its copies have landed, before the barrier that
+    // publishes the tile.
+    float lx = 0.f;
     auto issue = [&](int i) __attribute__((always_inline)) {
       const unsigned st = lbase + (unsigned)((i - qt0) & 1) * C::STAGE;
       copy_tile<C>(qh, st, i * C::T, N, bl, w);
       copy_tile<C>(oh, st + C::TB, i * C::T, N, bl, w);
       if (w == 0) {
-        // L of the tile's 32 queries (lanes 0..31), then D (lanes 32..63)
         const int r = min(i * C::T + l32, N - 1);
-        lds_copy4(h ? (const void*)(dh + r) : (const void*)(lh + r), st + 2 * C::TB);
+        lx = h ? dh[r] : lh[r];
+      }
+    };
+    auto publish = [&](int i) __attribute__((always_inline)) {
+      if (w == 0) {
+        const unsigned st = lbase + (unsigned)((i - qt0) & 1) * C::STAGE;
+        *(float LDS_AS*)((unsigned char LDS_AS*)0 + st + 2 * C::TB + 4 * lane) = h ? lx : lx * kLog2e;
       }
     };
     issue(qt0);
     wait_copies<0>();
+    publish(qt0);
     barrier();
     // V rows negated in place (once per key tile), so that dP - D comes out
     // of the matrix cores as D + dO (-V)^T with the accumulator started at D
@@ -483,14 +480,6 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         s = mfma(*(const bf16x8 LDS_AS*)(lds + rowa[kb] + QT), kr[kb], s);
         dp = mfma(*(const bf16x8 LDS_AS*)(lds + rowa[kb] + OT), *(const bf16x8 LDS_AS*)(lds + rowa[kb] + vw), dp);
       }
-      // L (as log2) of the lane's 16 queries
-      float lq[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 a = *(const f32x4 LDS_AS*)(lds + xa + XT + (8 * g + 4 * h) * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lq[4 * g + e] = a[e];
-      }
       // register r holds query q0 + 4h + rel, rel = 8*(r/4) + r%4: visible
       // iff rel <= N - 1 - (q0 + 4h) and (causal) rel >= key - (q0 + 4h)
       // a masked score becomes -inf: weight exp2(-inf) = 0 exactly (c > 0)
@@ -505,12 +494,19 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           if (rel > rhi || rel < rlo) s[r] = -INFINITY;
         }
       }
+      // P from L (log2 units) of the lane's 16 queries (read from LDS four
+      // at a time, next to their use)
       bf16x8 pb[2], dsb[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lq[r] * kLog2e));
-        pb[r >> 3][r & 7] = (__bf16)pv;
-        dsb[r >> 3][r & 7] = (__bf16)(pv * dp[r]);  // -dS
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 lg = *(const f32x4 LDS_AS*)(lds + xa + XT + (8 * g + 4 * h) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lg[e]));  // (L in log2 units)
+          pb[r >> 3][r & 7] = (__bf16)pv;
+          dsb[r >> 3][r & 7] = (__bf16)(pv * dp[r]);  // -dS
+        }
       }
       // dV^T += dO^T P and -dK^T += Q^T (-dS) (dO^T and Q^T by transpose reads)
 #pragma unroll
@@ -530,6 +526,7 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           dka[db] = mfma(qt, dsb[kq], dka[db]);
         }
       wait_copies<0>();
+      if (i + 1 < nq) publish(i + 1);
       barrier();
     };
     int i = qt0;
