@@ -140,7 +140,13 @@ def copy_calibration():
     for _ in range(5):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"[copy-cal] copied {n} bytes x5")
+    # the same bytes through an element-wise kernel (plain vector loads and
+    # stores, as the forward's own loads are), as a cross-check of the scale
+    srcf, dstf = src.view(torch.float32), dst.view(torch.float32)
+    for _ in range(5):
+        torch.add(srcf, 0.0, out=dstf)
+    torch.cuda.synchronize()
+    log(f"[copy-cal] copied {n} bytes x5 (device copy), then x5 (element-wise add of 0)")
 
 
 def measured_traffic(workload):
