@@ -14,6 +14,8 @@ causal, with Q/K/V already resident in HBM.  Prints ONE JSON line:
                           counters, null if the kernel source changed since)
   cpu_baseline            the fp64 CPU oracle timed on a bounded sample of
                           the same workload on this host's cores
+  cpu_baseline_native     the oracle's plain-C twin (fp64 tiled recurrence)
+                          timed the same way, as a second CPU baseline
 
 With --backward, a step is one ``fa_bwd`` call (dQ, dK, dV recomputed from
 the forward's O and LSE) on the same workload instead; FLOPs are counted as
@@ -212,6 +214,57 @@ def cpu_baseline(w, q, k, v, target_s):
         "sample": (f"{heads} whole head(s) ({nrows} query rows) of {w.name}, each row computed on its own "
                    f"by the fp64 numpy oracle (attention_rows_ref), {el:.1f} s wall; "
                    f"{cores} host cores visible, BLAS threads {blas_threads}"),
+    }
+
+
+def cpu_baseline_native(w, q, k, v, target_s):
+    """Time the oracle's plain-C twin (as it stands: fp64 tiled recurrence,
+    B_r = B_c = 64, one head per thread) on a bounded sample of the same
+    workload: a block of 256 consecutive query rows per head, at a position
+    that moves from head to head, heads in rounds of one per host core until
+    about ``target_s`` seconds have passed."""
+    import concurrent.futures
+
+    import numpy as np
+    import torch
+    from oracle import native  # CPU baseline leg only
+
+    lib = native.load()
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores, 16))
+    R = min(256, w.N)
+    flops = 0.0
+    blocks = 0
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def one(idx):
+        b, h = heads[idx % len(heads)]
+        r0 = (idx * 7919 * R) % max(1, w.N - R + 1)
+        qh, kh, vh = (x[b, h].to(torch.float64).numpy() for x in (q, k, v))
+        native.tiled_rows_c(qh, kh, vh, w.scale, w.causal, 64, 64, r0, r0 + R, lib=lib)
+        rows = np.arange(r0, r0 + R)
+        keys = (rows + 1) if w.causal else np.full(R, w.N)
+        return 4.0 * float(keys.sum()) * w.d
+
+    t0 = time.perf_counter()
+    el = 0.0
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        idx = 0
+        while el < target_s:
+            for f in list(ex.map(one, range(idx, idx + workers))):
+                flops += f
+            idx += workers
+            blocks += workers
+            el = time.perf_counter() - t0
+    return {
+        "value": flops / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(workers),
+        "kind": "oracle (plain C twin, tiled fp64)",
+        "cpu": cpu_model(),
+        "sample": (f"{blocks} blocks of {R} consecutive query rows (one per head, position varying by head) of "
+                   f"{w.name}, the fp64 tiled recurrence in C (oracle/tiled_ref.c, B_r = B_c = 64, gcc -O2), "
+                   f"{workers} threads, {el:.1f} s wall"),
     }
 
 
@@ -641,6 +694,7 @@ def main():
     traffic = None if args.backward else measured_traffic(w.name)
 
     cpu = None
+    cpu_native = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on a sample (~{args.cpu_seconds:.0f} s)")
         if args.backward:
@@ -648,6 +702,9 @@ def main():
         else:
             cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
         log(f"[bench] cpu baseline {cpu['value'] * 1e3:.3f} GFLOP/s ({cpu['sample']})")
+        if not args.backward:
+            cpu_native = cpu_baseline_native(w, q, k, v, args.cpu_seconds / 2)
+            log(f"[bench] cpu baseline (C twin) {cpu_native['value'] * 1e3:.3f} GFLOP/s ({cpu_native['sample']})")
 
     metric = "attn fwd TFLOP/s + % bf16 MFMA peak, N=16K d=128 causal (1 MI355X)"
     if args.backward:
@@ -672,6 +729,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic},
         "cpu_baseline": cpu,
+        # the oracle's plain-C twin timed the same way (a second CPU baseline)
+        "cpu_baseline_native": cpu_native,
         # per-launch kernel times (HIP events on the launch stream) and the device they ran on
         "kernel_ms": {"avg": round(avg_ms, 4), "median": round(med_ms, 4), "min": round(launch_ms[0], 4)},
         "device": {"arch": props.gcnArchName, "cus": props.multi_processor_count},

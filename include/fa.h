@@ -117,6 +117,19 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 const char* fa_strerror(int status);
 
 /*
+ * Whether the forward entry points take head dimension d with element type
+ * dtype (FA_DTYPE_BF16: fa_fwd, fa_fwd_ex, fa_fwd_split, fa_bwd;
+ * FA_DTYPE_F32: fa_fwd_f32): 1 if so, 0 if not (any other d or dtype).
+ * A pure host query; no HIP call.  The head dimensions are those of the
+ * pages' kernels ("15. FlashAttention", section "The kernel": the head
+ * dimension is a compile-time block size; "FlashAttention V1", section "4.
+ * Memory Analysis": d = 64 and 128 are the sizes analysed).
+ */
+#define FA_DTYPE_BF16 0
+#define FA_DTYPE_F32 1
+int fa_supported(int d, int dtype);
+
+/*
  * Host-side argument check of fa_fwd / fa_fwd_f32 without any HIP call:
  * returns the status those entry points would return before launching.
  * elem_bytes is 2 (bf16) or 4 (fp32).  Lets tests and callers validate on

@@ -27,8 +27,11 @@ FA_ERR_ALIGN = 7
 FA_ERR_VARIANT = 8
 FA_ERR_SCRATCH = 9
 FA_SPLIT_NOALLOC_BYTES = 32 << 20
+FA_DTYPE_BF16 = 0
+FA_DTYPE_F32 = 1
 
 EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_fwd_ex", "fa_fwd_split", "fa_fwd_split_noalloc", "fa_bwd", "fa_strerror",
+            "fa_supported",
             "fa_check_args", "fa_check_args_ex", "fa_check_args_split", "fa_split_chunks", "fa_bwd_check_args")
 
 _lib = None
@@ -65,6 +68,8 @@ def load_library(path=None):
     lib.fa_fwd_f32.restype = i
     lib.fa_strerror.argtypes = [i]
     lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_supported.argtypes = [i, i]
+    lib.fa_supported.restype = i
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i]
     lib.fa_check_args.restype = i
     lib.fa_fwd_ex.argtypes = [vp] * 5 + [i, i, i, i, i, i, f, i, i, i, vp]
@@ -174,6 +179,11 @@ def fa_bwd_check_args(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, scal
 
 def fa_strerror(status):
     return load_library().fa_strerror(int(status)).decode()
+
+
+def fa_supported(d, dtype):
+    """1 if the library takes head dimension d with FA_DTYPE_BF16 / FA_DTYPE_F32 inputs, else 0."""
+    return int(load_library().fa_supported(int(d), int(dtype)))
 
 
 def fa_check_args(q, k, v, o, lse, B, H, N, d, scale, causal, elem_bytes):

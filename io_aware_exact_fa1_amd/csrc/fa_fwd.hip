@@ -1095,6 +1095,10 @@ extern "C" int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, f
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+extern "C" int fa_supported(int d, int dtype) {
+  return (d == 64 || d == 128) && (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F32) ? 1 : 0;
+}
+
 extern "C" const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "ok";

@@ -13,6 +13,9 @@ its Python binding never do, and the oracle never imports them.
   * ``variants`` - grouped K/V heads, queries at an offset into a longer
                 key sequence, a sliding window, and split-KV partials with
                 their merge.
+  * ``native`` - the tiled recurrence in plain C (``tiled_ref.c``, fp64),
+                loaded through ctypes; imported on its own (``from oracle
+                import native``), not from here.
 """
 
 from .ref import as_f64, scores_ref, probabilities_ref, attention_ref, attention_rows_ref

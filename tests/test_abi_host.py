@@ -27,7 +27,7 @@ def test_header_declares_the_abi():
     assert declared_functions() == sorted(["fa_bwd", "fa_bwd_check_args", "fa_check_args", "fa_check_args_ex",
                                            "fa_check_args_split", "fa_fwd", "fa_fwd_ex", "fa_fwd_f32",
                                            "fa_fwd_split", "fa_fwd_split_noalloc", "fa_split_chunks",
-                                           "fa_strerror"])
+                                           "fa_strerror", "fa_supported"])
 
 
 def test_binding_exports_match_the_header():
@@ -41,6 +41,22 @@ def test_library_loads_and_exports_every_declared_symbol():
     raw = ctypes.CDLL(fa.LIB_PATH)
     for name in declared_functions():
         assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value, name
+
+
+def test_supported_head_dims_and_types():
+    for dtype in (fa.FA_DTYPE_BF16, fa.FA_DTYPE_F32):
+        assert fa.fa_supported(64, dtype) == 1
+        assert fa.fa_supported(128, dtype) == 1
+        for d in (0, 1, 32, 63, 65, 96, 127, 129, 256, -64):
+            assert fa.fa_supported(d, dtype) == 0, (d, dtype)
+    for dtype in (-1, 2, 3, 99):
+        assert fa.fa_supported(128, dtype) == 0
+    # the checks agree: a supported head dimension passes, any other is FA_ERR_HEAD_DIM
+    for d in (32, 64, 96, 128, 256):
+        st = fa.fa_check_args(Q, K, V, O, L, 1, 1, 8, d, 0.125, 0, 2)
+        assert (st == fa.FA_OK) == bool(fa.fa_supported(d, fa.FA_DTYPE_BF16)), d
+        if st != fa.FA_OK:
+            assert st == fa.FA_ERR_HEAD_DIM
 
 
 def test_strerror_covers_codes():
