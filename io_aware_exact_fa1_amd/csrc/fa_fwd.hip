@@ -123,7 +123,16 @@ struct Cfg {
   // stage offsets are folded into the 16-bit offset field of the LDS reads
   static_assert((NST - 1) * KT + (SB - 1) * 32 * ROWB < 65536, "K read offset range");
   static_assert((NST - 1) * KT + (PB - 1) * 16 * ROWB < 65536, "V read offset range");
-  static_assert(LDSB <= 160 * 1024, "LDS size");
+  // The epilogue stages each wave's O tile (32 rows x D, bf16) in LDS so that
+  // its global stores are whole rows.  The staging area starts at V stage 2:
+  // the next query tile's first copies fill only K stages 0..2 and V stages
+  // 0..1 before its first barrier, so the area is free until every wave has
+  // passed that barrier, i.e. finished its epilogue.
+  static constexpr int OBASE = VBASE + 2 * KT;
+  static constexpr int OROWS = 32 * ROWB;                  // one wave's staged O tile
+  static constexpr int LDS_TOTAL = OBASE + BR * ROWB > LDSB ? OBASE + BR * ROWB : LDSB;
+  static_assert(NST == 4 && (VCOPY ? 3 : 2) <= 3, "prologue copies stay below the staging area");
+  static_assert(LDS_TOTAL <= 160 * 1024, "LDS size");
 };
 
 
@@ -859,8 +868,20 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
           *(float4*)(orow + 32 * db + 8 * a + 4 * h) = ov;
         }
       if (h == 0) ex.ws_lse[prow] = empty ? -INFINITY : (m + __log2f(lt)) * kLn2;
-    } else if (query < Nq) {
-      uint16_t* orow = o + hoff + (size_t)query * C::D;
+    } else if (!split_mode) {
+      // O (bf16, RNE) through this wave's LDS staging area: row-major with
+      // the 16-byte chunks of row r XOR-swizzled by (r / rows per 256 bytes)
+      // so that the 8-byte writes spread over the banks; read back as whole
+      // rows, 64 lanes x 16 bytes (1 KB, 256 / ROWB * 4 rows) per store.
+      // Only this wave reads what it wrote, so no barrier is needed.
+      constexpr int CPR = C::CPR;               // 16-byte chunks per row
+      constexpr int RP2 = 256 / C::ROWB;        // rows per 256 bytes (1 or 2)
+      // (the lane index is made opaque so that these addresses are computed
+      // here, not hoisted out of the query-tile loop into live registers)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      unsigned char LDS_AS* stg_o = smem + C::OBASE + w * C::OROWS;
+      const int r0 = ln & 31, sw = (r0 / RP2) & (CPR - 1);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -868,9 +889,18 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
           bf16x4 ov;
 #pragma unroll
           for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc[db][4 * a + e] * inv);
-          *(u32x2*)(orow + 32 * db + 8 * a + 4 * h) = __builtin_bit_cast(u32x2, ov);
+          *(u32x2 LDS_AS*)(stg_o + r0 * C::ROWB + 16 * ((4 * db + a) ^ sw) + 8 * (ln >> 5)) =
+              __builtin_bit_cast(u32x2, ov);
         }
-      if (h == 0) lse[(size_t)bh * Nq + query] = (m + __log2f(lt)) * kLn2;
+      constexpr int RPS = 64 / CPR;             // rows per store instruction
+#pragma unroll
+      for (int i = 0; i < 32 / RPS; ++i) {
+        const int r = i * RPS + ln / CPR;       // row within the wave's 32
+        const int ch = ln % CPR;
+        const u32x4 x = *(const u32x4 LDS_AS*)(stg_o + r * C::ROWB + 16 * (ch ^ ((r / RP2) & (CPR - 1))));
+        if (qw0 + r < Nq) *(u32x4*)(o + hoff + (size_t)(qw0 + r) * C::D + 8 * ch) = x;
+      }
+      if (h == 0 && query < Nq) lse[(size_t)bh * Nq + query] = (m + __log2f(lt)) * kLn2;
     }
   }
 }
@@ -882,7 +912,7 @@ fa_fwd_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
                    int N, int T_r, int units_per_head, int num_units, int per_xcd, float c,
                    unsigned int qsign, ExtArgs ex) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDSB];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_TOTAL];
   fwd_unit<C, CAUSAL, EXT>(q, k, v, o, lse, N, T_r, units_per_head, num_units, per_xcd, c, qsign, ex,
                            (unsigned char LDS_AS*)smem);
 }
