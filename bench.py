@@ -92,6 +92,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sample-power", action="store_true",
+                   help="sample board power and the shader clock (amd-smi) during the timed steps; "
+                        "use enough --steps for a few seconds of run time")
     p.add_argument("--backward", action="store_true",
                    help="time the backward pass (fa_bwd) instead of the forward")
     p.add_argument("--shapes", default=None,
@@ -149,6 +152,54 @@ def copy_calibration():
         torch.add(srcf, 0.0, out=dstf)
     torch.cuda.synchronize()
     log(f"[copy-cal] copied {n} bytes x5 (device copy), then x5 (element-wise add of 0)")
+
+
+class PowerSampler:
+    """Board power and shader clock from ``amd-smi metric -p -c`` every
+    ~0.25 s on a background thread; samples at an idle clock (the GPU not
+    yet or no longer busy) are dropped."""
+
+    def __init__(self):
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _one(self):
+        import re
+        import subprocess
+        try:
+            out = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True,
+                                 timeout=5).stdout
+        except (OSError, subprocess.SubprocessError):
+            return None
+        pw = re.search(r"SOCKET_POWER:\s*([\d.]+)\s*W", out)
+        ck = re.search(r"^\s*CLK:\s*([\d.]+)\s*MHz", out, re.M)
+        return (float(pw.group(1)), float(ck.group(1))) if pw and ck else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            x = self._one()
+            if x and x[1] >= 500:
+                self.samples.append(x)
+            self._stop.wait(0.25)
+
+    def __enter__(self):
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        w = sorted(x[0] for x in self.samples)
+        c = sorted(x[1] for x in self.samples)
+        return {"samples": len(w), "socket_w_median": w[len(w) // 2], "socket_w_max": w[-1],
+                "sclk_mhz_median": c[len(c) // 2], "sclk_mhz_min": c[0],
+                "source": "amd-smi metric -p -c, every ~0.25 s during the timed steps"}
 
 
 def measured_traffic(workload):
@@ -672,6 +723,9 @@ def main():
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize()
+    sampler = PowerSampler() if args.sample_power else None
+    if sampler:
+        sampler.__enter__()
     t0 = time.perf_counter()
     for i in range(args.steps):
         evs[i][0].record(stream)
@@ -679,6 +733,8 @@ def main():
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if sampler:
+        sampler.__exit__()
     launch_ms = sorted(a.elapsed_time(b) for a, b in evs)
     avg_ms = sum(launch_ms) / len(launch_ms)
     med_ms = launch_ms[len(launch_ms) // 2]
@@ -735,6 +791,8 @@ def main():
         "kernel_ms": {"avg": round(avg_ms, 4), "median": round(med_ms, 4), "min": round(launch_ms[0], 4)},
         "device": {"arch": props.gcnArchName, "cus": props.multi_processor_count},
     }
+    if sampler:
+        out["power"] = sampler.summary()
     print(json.dumps(out), flush=True)
 
 
