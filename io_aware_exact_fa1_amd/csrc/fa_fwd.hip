@@ -44,7 +44,8 @@
 //    for that tile (new reference, acc and l rescaled, weights formed
 //    again), so the weights stay bounded.
 //  * Exponentials are exp2 with log2(e) folded into the scale; m, l and the
-//    output accumulator stay in fp32 registers; O is divided by l once.
+//    output accumulator stay in fp32 registers; O is divided by l once and
+//    staged through LDS, so that its global stores are whole rows.
 //  * Work units are query tiles (causal: a heavy tile paired with a light
 //    one, so every unit costs the same); the 1-D grid is remapped so that
 //    each XCD runs a contiguous range of units, i.e. the query tiles of the
