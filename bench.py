@@ -202,6 +202,19 @@ class PowerSampler:
                 "source": "amd-smi metric -p -c, every ~0.25 s during the timed steps"}
 
 
+def max_sclk_mhz():
+    """The device's maximum shader clock as amd-smi reports it (MAX_CLK of
+    GFX_0), or None where amd-smi is not available."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-c"], capture_output=True, text=True, timeout=10).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    m = re.search(r"^\s*MAX_CLK:\s*([\d.]+)\s*MHz", out, re.M)
+    return float(m.group(1)) if m else None
+
+
 def measured_traffic(workload):
     """HBM bytes per launch from the committed profiler counters
     (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy's reading), or
@@ -259,6 +272,8 @@ def cpu_baseline(w, q, k, v, target_s):
     return {
         "value": flops / el / 1e12,
         "unit": "TFLOP/s",
+        # the whole workload at the sampled rate: an extrapolation, not a measurement
+        "full_workload_estimate_s": round(w.flops / (flops / el), 1),
         "cores": int(min(threads, cores)),
         "kind": "oracle",
         "cpu": cpu_model(),
@@ -789,7 +804,7 @@ def main():
         "cpu_baseline_native": cpu_native,
         # per-launch kernel times (HIP events on the launch stream) and the device they ran on
         "kernel_ms": {"avg": round(avg_ms, 4), "median": round(med_ms, 4), "min": round(launch_ms[0], 4)},
-        "device": {"arch": props.gcnArchName, "cus": props.multi_processor_count},
+        "device": {"arch": props.gcnArchName, "cus": props.multi_processor_count, "max_sclk_mhz": max_sclk_mhz()},
     }
     if sampler:
         out["power"] = sampler.summary()
