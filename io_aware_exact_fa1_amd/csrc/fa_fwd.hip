@@ -29,13 +29,15 @@
 //    read from a row-major V tile in LDS with ds_read_b64_tr_b16, the gfx950
 //    LDS transpose load.
 //  * K and V tiles are copied HBM -> LDS with global_load_lds_dwordx4
-//    (no VGPR staging) into a ring of four LDS stages, two tiles ahead of
-//    their use, with an XOR swizzle of the 16-byte chunks so that both the
-//    K reads and the transposed V reads hit distinct LDS banks.
+//    (no VGPR staging) into a ring of four LDS stages, issued two (d = 64)
+//    or three (d = 128) tiles ahead of their use, with an XOR swizzle of the
+//    16-byte chunks so that both the K reads and the transposed V reads hit
+//    distinct LDS banks.
 //  * Each step of a wave is a matrix-core phase (S_j = K_j Q^T and
 //    acc += V_{j-1}^T P_{j-1}^T) and a vector-ALU phase (softmax of S_j).
 //    The two waves of a SIMD run one phase apart, so one feeds the matrix
-//    cores while the other computes exponentials.  In the matrix phase
+//    cores while the other computes exponentials (d = 128: one workgroup
+//    barrier per step; d = 64: one per phase).  In the matrix phase
 //    every LDS address is a per-lane offset computed once plus an
 //    immediate, so that phase issues no vector-ALU work at all.
 //  * The exponent reference of a row is fixed after its first key tile, so
@@ -44,8 +46,10 @@
 //    for that tile (new reference, acc and l rescaled, weights formed
 //    again), so the weights stay bounded.
 //  * Exponentials are exp2 with log2(e) folded into the scale; m, l and the
-//    output accumulator stay in fp32 registers; O is divided by l once and
-//    staged through LDS, so that its global stores are whole rows.
+//    output accumulator stay in fp32 registers; O is divided once, by the
+//    sum of the bf16 weights that P V multiplied (l plus a correction taken
+//    on the tiles that dominate a row), and staged through LDS, so that its
+//    global stores are whole rows.
 //  * Work units are query tiles (causal: a heavy tile paired with a light
 //    one, so every unit costs the same); the 1-D grid is remapped so that
 //    each XCD runs a contiguous range of units, i.e. the query tiles of the
