@@ -93,8 +93,9 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sample-power", action="store_true",
-                   help="sample board power and the shader clock (amd-smi) during the timed steps; "
-                        "use enough --steps for a few seconds of run time")
+                   help="sample board power and the shader clock (amd-smi, run as a child process) during "
+                        "the timed steps; use enough --steps for a few seconds of run time, and not under "
+                        "a profiler")
     p.add_argument("--backward", action="store_true",
                    help="time the backward pass (fa_bwd) instead of the forward")
     p.add_argument("--shapes", default=None,
@@ -203,16 +204,19 @@ class PowerSampler:
 
 
 def max_sclk_mhz():
-    """The device's maximum shader clock as amd-smi reports it (MAX_CLK of
-    GFX_0), or None where amd-smi is not available."""
+    """The device's highest shader-clock DPM level in MHz, read from sysfs
+    (pp_dpm_sclk; no child process), or None where it is not readable."""
+    import glob
     import re
-    import subprocess
-    try:
-        out = subprocess.run(["amd-smi", "metric", "-c"], capture_output=True, text=True, timeout=10).stdout
-    except (OSError, subprocess.SubprocessError):
-        return None
-    m = re.search(r"^\s*MAX_CLK:\s*([\d.]+)\s*MHz", out, re.M)
-    return float(m.group(1)) if m else None
+    best = None
+    for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+        try:
+            with open(f) as fh:
+                for m in re.finditer(r"(\d+)\s*Mhz", fh.read(), re.I):
+                    best = max(best or 0.0, float(m.group(1)))
+        except OSError:
+            continue
+    return best
 
 
 def measured_traffic(workload):
