@@ -39,7 +39,10 @@
 //    cores while the other computes exponentials (d = 128: one workgroup
 //    barrier per step; d = 64: one per phase).  In the matrix phase
 //    every LDS address is a per-lane offset computed once plus an
-//    immediate, so that phase issues no vector-ALU work at all.
+//    immediate, so that phase issues no address arithmetic.  At d = 64,
+//    where the softmax of 128 keys is the longer phase, the bf16 packing of
+//    P_{j-1} (and its normaliser correction, below) moves into the matrix
+//    phase, beside the first products of S_j.
 //  * The exponent reference of a row is fixed after its first key tile, so
 //    the loop normally rescales nothing; a wave whose weights outgrow it by
 //    more than 2^16 in a tile takes the running-max step of the recurrence
@@ -231,6 +234,66 @@ __device__ __forceinline__ void prefetch_k(bf16x8 (&kpre)[C::KD][C::SB], const L
     for (int sb = 0; sb < C::SB; ++sb) kpre[kb][sb] = lds_k<C>(lo, kst, kb, sb);
 }
 
+// A lane's running sums over its keys of a row: lh = l / 2, where l is the
+// sum of the unrounded fp32 weights (LSE = m + log2 l; kept halved, an exact
+// scaling, so that the heavy-tile test below is one compare), and
+// corr = sum of (bf16(p) - p) over the tiles where it was taken.  O divides
+// by l + corr, the sum of the bf16 weights that P V multiplies, so that a
+// row dominated by one key gets that key's V row up to the bf16 rounding
+// of O.  (With the reference fixed at the first tile's max, a dominant
+// later weight is 2^rise, not 1 as under the running max: dividing by the
+// unrounded l would carry its bf16 rounding, up to 2^-8 relative, into O.)
+// The correction is taken on a tile only when the lane's weights of the
+// tile exceed half of what it summed before (a "heavy" tile; the branch is
+// wave-uniform, the correction per lane): a weight of a tile left out is
+// less than half of its row's final sum, so its rounding moves O by less
+// than 2^-9 |v|, and the weights that dominate a row are always corrected.
+struct RowSums {
+  float lh, corr;
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// P (fp32, in the score registers of block sb) to the bf16 operand of P V.
+template <class C>
+__device__ __forceinline__ void pack_block(const f32x16 (&s)[C::SB], bf16x8 (&pb)[C::PB], int sb) {
+#pragma unroll
+  for (int kb2 = 2 * sb; kb2 < 2 * sb + 2; ++kb2) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pb[kb2][j] = (__bf16)s[kb2 >> 1][8 * (kb2 & 1) + j];
+    pin(pb[kb2]);
+  }
+}
+
+// A tile's bf16 rounding correction of the normaliser (see RowSums): on a
+// heavy tile, corr += (sum of the bf16 weights) - ts, where ts is the sum of
+// the unrounded weights.  The branch is wave-uniform, the correction per
+// lane (a row's bits never depend on other rows).
+template <class C>
+__device__ __forceinline__ void heavy_corr(const bf16x8 (&pb)[C::PB], float ts, bool heavy, RowSums& sums) {
+  if (__builtin_amdgcn_ballot_w64(heavy) != 0) {
+    // sum of the bf16 weights, v_dot2c_f32_bf16 against (1, 1)
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float tb[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kb2 = 0; kb2 < C::PB; ++kb2) {
+      tb[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 0, 1), one2, tb[0], false);
+      tb[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 2, 3), one2, tb[1], false);
+      tb[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 4, 5), one2, tb[0], false);
+      tb[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 6, 7), one2, tb[1], false);
+    }
+    sums.corr += heavy ? (tb[0] + tb[1]) - ts : 0.f;
+  }
+}
+
+// A tile's weights not yet packed: the matrix phase that multiplies them
+// packs them and takes the heavy-tile correction (the two-barrier schedule,
+// d = 64, where the softmax is the longer phase).
+struct PendingP {
+  float ts;    // this lane's sum of the tile's unrounded weights
+  bool heavy;  // ts > half of what the lane summed before the tile
+};
+
 // The matrix-core phase of one step: S = K Q^T (HAS_QK, K tile at stage
 // offset kst) and acc += V^T P^T (HAS_PV, V tile at stage offset vst).
 // LDS operands are read a few MFMAs ahead of their use (two k-steps for K,
@@ -238,11 +301,16 @@ __device__ __forceinline__ void prefetch_k(bf16x8 (&kpre)[C::KD][C::SB], const L
 // the LDS latency hides behind the matrix cores; the first KD k-steps of K
 // come in kpre, read during the preceding phase.  With kst / vst known at
 // compile time, every LDS address is a precomputed lane offset plus an
-// immediate: this phase issues no vector-ALU instruction and no copy.
-template <class C, bool HAS_QK, bool HAS_PV>
+// immediate: this phase issues no address arithmetic and no copy.
+// PACKIN (with HAS_PV): s arrives holding the fp32 weights of the previous
+// tile, which this phase packs into pb (each score block just before the
+// first product that overwrites it) and corrects the normaliser for
+// (heavy_corr), so that the vector phase, the longer one at d = 64, ends
+// with the exponentials and their sum.
+template <class C, bool HAS_QK, bool HAS_PV, bool PACKIN = false>
 __device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& lo, const bf16x8 (&qr)[C::KB],
-                                       f32x16 (&s)[C::SB], const bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB],
-                                       const bf16x8 (&kpre)[C::KD][C::SB]) {
+                                       f32x16 (&s)[C::SB], bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB],
+                                       const bf16x8 (&kpre)[C::KD][C::SB], RowSums& sums, const PendingP& pend) {
   const unsigned char LDS_AS* lds = (const unsigned char LDS_AS*)0;
   auto load_k = [&](int kb, int sb) -> bf16x8 { return lds_k<C>(lo, kst, kb, sb); };
   constexpr int NV = C::PB * C::DB;  // V operands (one per P V instruction)
@@ -269,12 +337,21 @@ __device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& l
     for (int i = 0; i < VD && i < NV; ++i) va[i] = load_v(i);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // PACKIN: s holds the previous tile's fp32 weights; each block is packed
+  // into pb just before the first product of this tile overwrites it
+  constexpr bool PK = PACKIN && HAS_PV;
+  if (PK && !HAS_QK) {
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb) pack_block<C>(s, pb, sb);
+  }
   if (HAS_QK) {
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
-      for (int sb = 0; sb < C::SB; ++sb)
+      for (int sb = 0; sb < C::SB; ++sb) {
+        if (PK && kb == 0) pack_block<C>(s, pb, sb);
         s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][sb], qr[kb], kb == 0 ? zero : s[sb], 0, 0, 0);
+      }
       if (kb + KD < C::KB) {
 #pragma unroll
         for (int sb = 0; sb < C::SB; ++sb) ka[kb + KD][sb] = load_k(kb + KD, sb);
@@ -287,6 +364,10 @@ __device__ __forceinline__ void tile_m(int kst, int vst, const LaneOffsets<C>& l
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  if (PK) {
+    heavy_corr<C>(pb, pend.ts, pend.heavy, sums);
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (HAS_PV) {
 #pragma unroll
@@ -317,24 +398,6 @@ __device__ __forceinline__ float tile_rowmax(const f32x16 (&s)[C::SB]) {
 // to the running max m_new = max(m, mxs), and l and acc are multiplied by
 // exp2(m - m_new).  Other rows keep every bit as it is, so that a row's
 // result never depends on what other rows of its wave see.
-// A lane's running sums over its keys of a row: lh = l / 2, where l is the
-// sum of the unrounded fp32 weights (LSE = m + log2 l; kept halved, an exact
-// scaling, so that the heavy-tile test below is one compare), and
-// corr = sum of (bf16(p) - p) over the tiles where it was taken.  O divides
-// by l + corr, the sum of the bf16 weights that P V multiplies, so that a
-// row dominated by one key gets that key's V row up to the bf16 rounding
-// of O.  (With the reference fixed at the first tile's max, a dominant
-// later weight is 2^rise, not 1 as under the running max: dividing by the
-// unrounded l would carry its bf16 rounding, up to 2^-8 relative, into O.)
-// The correction is taken on a tile only when the lane's weights of the
-// tile exceed half of what it summed before (a "heavy" tile; the branch is
-// wave-uniform, the correction per lane): a weight of a tile left out is
-// less than half of its row's final sum, so its rounding moves O by less
-// than 2^-9 |v|, and the weights that dominate a row are always corrected.
-struct RowSums {
-  float lh, corr;
-};
-
 template <class C>
 __device__ __forceinline__ void raise_ref(bool up, float mxs, float& m, RowSums& sums, f32x16 (&acc)[C::DB]) {
   const float m_new = up ? __builtin_fmaxf(m, mxs) : m;
@@ -367,9 +430,10 @@ __device__ __forceinline__ float tile_exp(f32x16 (&s)[C::SB], float c, float mre
 // The vector-ALU phase: online softmax of one tile.  Mask (MASK: keys past
 // N, and keys after the query when causal, get -inf, i.e. weight exactly 0;
 // with a sliding window (wnd > 0) also keys before query - wnd + 1),
-// exponent reference, P = exp2(S*c - m_ref) into the bf16 operand pb, row
-// sum of the unrounded weights and, on heavy tiles, the bf16 rounding
-// correction into sums.
+// exponent reference, P = exp2(S*c - m_ref), row sum of the unrounded
+// weights; PACK: P into the bf16 operand pb and, on heavy tiles, the bf16
+// rounding correction into sums (otherwise both are left to the next matrix
+// phase, with the tile's sum and heavy flag in pend).
 //  * FIRST / MASK tiles compute their row max.  The reference is the max of
 //    the row's first tile with a visible key (a row that has seen none yet
 //    uses the safe reference 0); a row whose max in a masked tile rises more
@@ -382,10 +446,10 @@ __device__ __forceinline__ float tile_exp(f32x16 (&s)[C::SB], float c, float mre
 //    rows raise their reference to the running max, and every row forms its
 //    weights again (unchanged bits for the other rows: same scores, same
 //    reference).
-template <class C, bool CAUSAL, bool MASK, bool FIRST, class Rescore>
+template <class C, bool CAUSAL, bool MASK, bool FIRST, bool PACK, class Rescore>
 __device__ __forceinline__ void tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C::PB], f32x16 (&acc)[C::DB],
-                                             float& m, RowSums& sums, int k0, int qw0, int N, float c, int lane,
-                                             int wnd, Rescore&& rescore) {
+                                             float& m, RowSums& sums, PendingP& pend, int k0, int qw0, int N,
+                                             float c, int lane, int wnd, Rescore&& rescore) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
   // register i of block sb holds key k0 + 32*sb + 8*(i/4) + 4h + i%4
@@ -433,27 +497,15 @@ __device__ __forceinline__ void tile_softmax(f32x16 (&s)[C::SB], bf16x8 (&pb)[C:
       ts = tile_exp<C>(s, c, m);
     }
   }
-#pragma unroll
-  for (int kb2 = 0; kb2 < C::PB; ++kb2) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) pb[kb2][j] = (__bf16)s[kb2 >> 1][8 * (kb2 & 1) + j];
-    pin(pb[kb2]);
-  }
   const bool heavy = ts > sums.lh;
-  if (__builtin_amdgcn_ballot_w64(heavy) != 0) {
-    // heavy tile: sum of the bf16 weights, v_dot2c_f32_bf16 against (1, 1)
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-    float tb[2] = {0.f, 0.f};
+  if (PACK) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < C::PB; ++kb2) {
-      tb[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 0, 1), one2, tb[0], false);
-      tb[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 2, 3), one2, tb[1], false);
-      tb[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 4, 5), one2, tb[0], false);
-      tb[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[kb2], pb[kb2], 6, 7), one2, tb[1], false);
-    }
-    // (only the heavy lanes: a row's bits never depend on other rows)
-    sums.corr += heavy ? (tb[0] + tb[1]) - ts : 0.f;
+    for (int sb = 0; sb < C::SB; ++sb) pack_block<C>(s, pb, sb);
+    heavy_corr<C>(pb, ts, heavy, sums);
+  } else {
+    // (packed, and corrected when heavy, by the next matrix phase)
+    pend.ts = ts;
+    pend.heavy = heavy;
   }
   sums.lh = fmaf(ts, 0.5f, sums.lh);  // (exact scaling by a power of two)
   pin(sums.lh);
@@ -635,6 +687,8 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     const unsigned mdst = lo.base + (lag ? C::VBASE : 0u);  // ... and its LDS ring
     f32x16 s[C::SB];
     bf16x8 p[C::PB];  // P_{j-1} is read in M(j), then P_j is written in V(j)
+    // (two-barrier schedule: V(j) leaves P_j unpacked in s; M(j+1) packs it)
+    PendingP pend{0.f, false};
     bf16x8 kpre[C::KD][C::SB];
     // S_j = K_j Q^T once more, from the K tile at stage offset kst (still in
     // LDS during the vector phase of step j): the rare path of tile_softmax
@@ -655,7 +709,7 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         if (j + 2 < nkv) load_tile<C>(msrc, mdst + dst, ktile(j + 2) * C::BC, Nk, lo, w);
         if (QK) prefetch_k<C>(kpre, lo, kst);
       }
-      tile_m<C, QK, PV>(kst, vst, lo, qr, s, p, acc, kpre);
+      tile_m<C, QK, PV, !VC>(kst, vst, lo, qr, s, p, acc, kpre, sums, pend);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) pin(acc[db]);
 #pragma unroll
@@ -672,8 +726,8 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
     auto vphase = [&](int j, int kst0, int dst, int kst1, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(mask_tag)::value;
       constexpr bool FIRST = decltype(first_tag)::value;
-      tile_softmax<C, CAUSAL, MASK, FIRST>(s, p, acc, m, sums, ktile(j) * C::BC, qoff + qw0, Nk, c, lane, wnd,
-                                           [&]() __attribute__((always_inline)) { rescore_at(kst0); });
+      tile_softmax<C, CAUSAL, MASK, FIRST, VC>(s, p, acc, m, sums, pend, ktile(j) * C::BC, qoff + qw0, Nk, c,
+                                               lane, wnd, [&]() __attribute__((always_inline)) { rescore_at(kst0); });
       __builtin_amdgcn_sched_barrier(0);
       if (VC) {
         if (j + 3 < nkv) {
@@ -711,7 +765,7 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
       // the leading P V of tile t in window t+1 -- come after it.
       auto m1 = [&](int kst, int vst, auto has_qk, auto has_pv) __attribute__((always_inline)) {
         constexpr bool QK = decltype(has_qk)::value, PV = decltype(has_pv)::value;
-        tile_m<C, QK, PV>(kst, vst, lo, qr, s, p, acc, kpre);
+        tile_m<C, QK, PV>(kst, vst, lo, qr, s, p, acc, kpre, sums, pend);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) pin(acc[db]);
 #pragma unroll
@@ -726,8 +780,8 @@ fwd_unit(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u
         constexpr bool LAG = decltype(lag_tag)::value;
         constexpr bool MASK = decltype(mask_tag)::value;
         constexpr bool FIRST = decltype(first_tag)::value;
-        tile_softmax<C, CAUSAL, MASK, FIRST>(s, p, acc, m, sums, ktile(j) * C::BC, qoff + qw0, Nk, c, lane, wnd,
-                                             [&]() __attribute__((always_inline)) { rescore_at(s0); });
+        tile_softmax<C, CAUSAL, MASK, FIRST, true>(s, p, acc, m, sums, pend, ktile(j) * C::BC, qoff + qw0, Nk, c,
+                                                   lane, wnd, [&]() __attribute__((always_inline)) { rescore_at(s0); });
         __builtin_amdgcn_sched_barrier(0);
         const int ct = LAG ? j + 2 : j + 3;  // the tile this wave copies now
         if (ct < nkv) {
