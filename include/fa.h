@@ -89,9 +89,14 @@ enum fa_status {
  * Arithmetic: Q K^T and P V run on bf16 matrix cores with fp32 accumulation;
  * the row max, the exponentials (base 2 with log2(e) folded into the scale),
  * the row sums, the running output and LSE are fp32; P is rounded to bf16
- * only as the operand of P V, while l sums the unrounded values.  The
- * exponent reference of a row is the max of its first key tile (any common
- * reference gives the same O and LSE in exact arithmetic); on a tile where
+ * only as the operand of P V, while l sums the unrounded values and gives
+ * LSE.  O is divided by the sum of the rounded weights P V multiplied: l
+ * plus, on the tiles whose weights dominate a row, the difference between
+ * the rounded and the unrounded weights ("15. FlashAttention", section "The
+ * kernel": fp32 statistics, p cast to the value type for P V).  The
+ * exponent reference of a row is the max of its first key tile with a
+ * visible key (any common reference gives the same O and LSE in exact
+ * arithmetic); on a tile where
  * a row's weights would outgrow it by more than 2^16, that row takes the
  * running-max step of the recurrence ("15. FlashAttention", section "Online
  * softmax: normalize as you go": new reference, l and the accumulator
